@@ -1,0 +1,55 @@
+"""Compile the gfx950 HIP sources in csrc/ into the in-tree shared library libattn.so.
+
+Every call recompiles (the object files are cheap to rebuild and this keeps the library in
+step with its sources). Used by ``__graft_entry__.build()`` and ``python -m
+exact_tiled_attention_25_amd.build``.
+"""
+import concurrent.futures
+import glob
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+OBJDIR = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libattn.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+# -packed-fp32-ops: never emit v_pk_{add,mul,fma}_f32 (hipcc's host pass warns that it does
+# not know the feature; that warning is harmless).
+FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         f"-I{os.path.join(ROOT, 'include')}"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines()
+                    if "packed-fp32-ops" not in l and "hip-link" not in l and l.strip())
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose=False, jobs=None):
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    os.makedirs(OBJDIR, exist_ok=True)
+    objs = [os.path.join(OBJDIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        outs = list(ex.map(lambda so: _run([HIPCC, *FLAGS, "-c", so[0], "-o", so[1]]), zip(srcs, objs)))
+    tmp = LIB + ".tmp"
+    outs.append(_run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]))
+    os.replace(tmp, LIB)
+    if verbose:
+        for o in outs:
+            if o:
+                print(o)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

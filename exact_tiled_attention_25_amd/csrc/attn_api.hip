@@ -1,0 +1,140 @@
+// C ABI of libattn.so: argument validation, device check and dispatch to the kernels.
+// Nothing here allocates, synchronises or touches tensor contents on the host.
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "../../include/attn.h"
+#include "attn_launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+attn_status_t check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ATTN_EDEVICE;
+  if (dev < kMaxDevices) {
+    const int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (st == 1) return ATTN_OK;
+    if (st == 2) return ATTN_EDEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_EDEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? ATTN_OK : ATTN_EDEVICE;
+}
+
+bool supported_d(int d) { return d == 64 || d == 128 || d == 256; }
+
+// Sizes shared by every entry point. Byte offsets inside one batch slice are 32-bit
+// (buffer addressing), so a batch slice of a 16-bit tensor must stay below 2^31 bytes.
+attn_status_t check_sizes(int B, int H, int N, int d, bool* empty) {
+  if (B < 0 || H < 0 || N < 0) return ATTN_EINVAL;
+  if (!supported_d(d)) return ATTN_EUNSUPPORTED;
+  *empty = (B == 0 || H == 0 || N == 0);
+  if (*empty) return ATTN_OK;
+  const double slice = (double)N * H * d * 2.0;
+  if (slice >= 2147483648.0 - 65536.0 * H * d) return ATTN_EUNSUPPORTED;
+  if ((double)B * H * ((N + 127) / 128) >= 2147483647.0) return ATTN_EUNSUPPORTED;
+  return ATTN_OK;
+}
+
+bool bad_scale(float scale) { return !std::isfinite(scale) || scale < 0.f; }
+
+attn_status_t launched(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ELAUNCH; }
+
+constexpr double kLog2e = 1.4426950408889634074;
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int N, int d, int causal, float scale,
+                       attn_dtype_t dtype, attn_stream_t stream) {
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_EINVAL;
+  if (bad_scale(scale)) return ATTN_EINVAL;
+  bool empty = false;
+  attn_status_t st = check_sizes(B, H, N, d, &empty);
+  if (st != ATTN_OK || empty) return st;
+  if (!q || !k || !v || !o || !lse) return ATTN_EINVAL;
+  if ((st = check_device()) != ATTN_OK) return st;
+  attn::FwdParams p{q, k, v, o, lse, B, H, N, (float)(scale * kLog2e)};
+  (void)hipGetLastError();
+  return launched(attn::launch_fwd(dtype == ATTN_BF16, d, causal != 0, p, (hipStream_t)stream));
+}
+
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d) {
+  (void)d;
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  return (size_t)B * H * N * sizeof(float);
+}
+
+attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                       int B, int H, int N, int d, int causal, float scale,
+                       attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                       attn_stream_t stream) {
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_EINVAL;
+  if (bad_scale(scale)) return ATTN_EINVAL;
+  bool empty = false;
+  attn_status_t st = check_sizes(B, H, N, d, &empty);
+  if (st != ATTN_OK || empty) return st;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_EINVAL;
+  if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, H, N, d)) return ATTN_EWORKSPACE;
+  if ((st = check_device()) != ATTN_OK) return st;
+  attn::BwdParams p{q, k, v, o, lse, dout, dq, dk, dv, (float*)workspace, B, H, N, scale,
+                    (float)(scale * kLog2e)};
+  (void)hipGetLastError();
+  return launched(attn::launch_bwd(dtype == ATTN_BF16, d, causal != 0, p, (hipStream_t)stream));
+}
+
+attn_status_t attn_fp8_quantize(const void* x, uint8_t* x8, float* descale,
+                                int B, int H, int N, int d, attn_dtype_t dtype,
+                                int rotate, uint64_t hadamard_seed, attn_stream_t stream) {
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_EINVAL;
+  bool empty = false;
+  attn_status_t st = check_sizes(B, H, N, d, &empty);
+  if (st != ATTN_OK || empty) return st;
+  if (!x || !x8 || !descale) return ATTN_EINVAL;
+  if ((st = check_device()) != ATTN_OK) return st;
+  attn::Fp8QuantParams p{x, x8, descale, B, H, N, rotate != 0, hadamard_seed};
+  (void)hipGetLastError();
+  return launched(attn::launch_fp8_quantize(dtype == ATTN_BF16, d, p, (hipStream_t)stream));
+}
+
+attn_status_t attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                           void* o, float* lse, int B, int H, int N, int d, int causal,
+                           float scale, const float* descale_q, const float* descale_k,
+                           const float* descale_v, uint64_t hadamard_seed,
+                           attn_dtype_t out_dtype, attn_stream_t stream) {
+  (void)hadamard_seed;  // scores do not depend on the (shared, orthogonal) rotation
+  if (out_dtype != ATTN_BF16 && out_dtype != ATTN_FP16) return ATTN_EINVAL;
+  if (bad_scale(scale)) return ATTN_EINVAL;
+  bool empty = false;
+  attn_status_t st = check_sizes(B, H, N, d, &empty);
+  if (st != ATTN_OK || empty) return st;
+  if (!q8 || !k8 || !v8 || !o || !lse || !descale_q || !descale_k || !descale_v) return ATTN_EINVAL;
+  if ((st = check_device()) != ATTN_OK) return st;
+  attn::Fp8FwdParams p{q8, k8, v8, descale_q, descale_k, descale_v, o, lse, B, H, N,
+                       (float)(scale * kLog2e)};
+  (void)hipGetLastError();
+  return launched(attn::launch_fwd_fp8(out_dtype == ATTN_BF16, d, causal != 0, p, (hipStream_t)stream));
+}
+
+const char* attn_strerror(attn_status_t s) {
+  switch (s) {
+    case ATTN_OK: return "success";
+    case ATTN_EINVAL: return "invalid argument (null pointer, negative size, bad scale or enum)";
+    case ATTN_EUNSUPPORTED: return "unsupported shape (head dim must be 64, 128 or 256; batch slice below 2 GiB)";
+    case ATTN_EWORKSPACE: return "workspace missing or too small (see attn_bwd_workspace_bytes)";
+    case ATTN_ELAUNCH: return "kernel launch failed";
+    case ATTN_EDEVICE: return "current device is not an MI355X-class gfx950 GPU";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// Device-side building blocks for the gfx950 attention kernels: vector types, the MFMA
+// forms used (32x32x16 bf16/f16, 32x32x64 f8f6f4), buffer resources, packed converts,
+// the cross-half lane swap and the XCD-aware block remap.
+//
+// MFMA register layouts (32x32 output tile, wave64; verified on the hardware):
+//   A (32 x K):  lane l holds row  l%32, its K-chunk (l/32); 8 bf16/f16 (or 32 fp8) per lane.
+//   B (K x 32):  lane l holds column l%32, the same K-chunk (l/32).
+//   C (32 x 32): lane l holds column l%32; accumulator r is row 8*(r/4) + 4*(l/32) + r%4.
+// A and B share their per-lane K mapping, so any consistent permutation of the contraction
+// index (head dim for Q K^T, keys for P V) is harmless; the kernels rely on that to feed the
+// score accumulator straight into the P V product (see attn_fwd.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Buffer resource word 3 for raw (untyped) gfx9 buffer accesses: DATA_FORMAT = 32 bit.
+// Loads past num_records return zero and stores past it are dropped.
+constexpr int kBufWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+}
+
+// 32x32x16 MFMA on 16-bit inputs held as 4 dwords per lane.
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma32x16(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Two floats -> two 16-bit values (round to nearest even) in one dword, first in the low half.
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  if constexpr (BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+// Combine a lane value with the same lane of the other wave half (lane l ^ 32).
+// permlane32_swap(x, x) returns r[0] = (x[0..31], x[0..31]) and r[1] = (x[32..63], x[32..63])
+// across the two halves, so r[0] op r[1] is the two-half reduction in every lane.
+__device__ __forceinline__ float xhalf_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Workgroups are handed to the 8 XCDs round-robin (block b runs on XCD b % 8). Give each XCD
+// a contiguous range of work items so that the query tiles of one head, which read the same
+// K and V, share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblk) {
+  const int q = nblk >> 3, r = nblk & 7;
+  const int x = bid & 7, i = bid >> 3;
+  return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
+}  // namespace attn

@@ -1,0 +1,61 @@
+// Internal launch interface between the C ABI (attn_api.hip) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, N;
+  float c;  // softmax scale * log2(e): scores are exponentiated with exp2
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // workspace: rowsum(dO o O), [B][H][N]
+  int B, H, N;
+  float scale;
+  float c;  // scale * log2(e)
+};
+
+struct Fp8QuantParams {
+  const void* x;
+  uint8_t* x8;
+  float* descale;
+  int B, H, N;
+  int rotate;
+  uint64_t seed;
+};
+
+struct Fp8FwdParams {
+  const uint8_t* q8;
+  const uint8_t* k8;
+  const uint8_t* v8;
+  const float* dq;
+  const float* dk;
+  const float* dv;
+  void* o;
+  float* lse;
+  int B, H, N;
+  float c;
+};
+
+hipError_t launch_fwd(bool bf16, int d, bool causal, const FwdParams& p, hipStream_t s);
+hipError_t launch_bwd(bool bf16, int d, bool causal, const BwdParams& p, hipStream_t s);
+hipError_t launch_fp8_quantize(bool bf16, int d, const Fp8QuantParams& p, hipStream_t s);
+hipError_t launch_fwd_fp8(bool out_bf16, int d, bool causal, const Fp8FwdParams& p, hipStream_t s);
+
+}  // namespace attn

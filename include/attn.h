@@ -1,0 +1,100 @@
+/* attn.h - exact tiled attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libattn.so. Every tensor pointer is DEVICE memory owned by the caller. The
+ * library allocates nothing, never synchronises the host, and enqueues all its work on the
+ * caller's stream in call order. Calls return after the launch; a status other than
+ * ATTN_OK means nothing was enqueued (argument and device errors) or the launch itself
+ * failed (ATTN_ELAUNCH). No C++ exception crosses this interface.
+ *
+ * Shapes and layout (the same for every entry point):
+ *   Q, K, V, O, dO, dQ, dK, dV : [B][N][H][d] contiguous ("token-major", row pitch H*d),
+ *                                 element type given by `dtype` (bf16 or fp16).
+ *   LSE                         : [B][H][N] fp32, natural-log log-sum-exp of each query row.
+ *   FP8 tensors                 : [B][N][H][d] OCP e4m3 bytes (E4M3FN: bias 7, max 448).
+ *   FP8 descales                : [B][H][ceil(N/64)] fp32; real value = e4m3 value * descale
+ *                                 of the 64-row block the row lies in.
+ * Sizes: B, H, N >= 0 (a zero size is an empty problem and returns ATTN_OK doing nothing);
+ * d in {64, 128, 256}; N need not be a multiple of any tile size. The causal mask lets
+ * query i see key j iff j <= i. `scale` must be finite and >= 0 (usually 1/sqrt(d)).
+ *
+ * Sources: the pages "FlashAttention-3: Hopper Asynchrony and FP8 Attention" (Symbol Map,
+ * Deep Dive, Putting It Together) and "FlashAttention 3 Hardware Acceleration: Hopper GPU
+ * Strategies for Long-Context Enterprise Inference Optimization" (FP8 sections).
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_FP8_BLOCK 64 /* rows per FP8 quantisation block */
+
+typedef enum { ATTN_BF16 = 0, ATTN_FP16 = 1 } attn_dtype_t;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_EINVAL = 1,        /* null pointer, negative size, non-finite or negative scale, bad enum */
+  ATTN_EUNSUPPORTED = 2,  /* d not in {64,128,256}, or a size whose indices overflow 32 bits */
+  ATTN_EWORKSPACE = 3,    /* workspace missing or smaller than attn_bwd_workspace_bytes() */
+  ATTN_ELAUNCH = 4,       /* the HIP runtime rejected a kernel launch */
+  ATTN_EDEVICE = 5        /* the current device is not gfx950 */
+} attn_status_t;
+
+/* A hipStream_t passed as an opaque pointer; NULL means the null stream. */
+typedef void* attn_stream_t;
+
+/* Forward exact attention: O = softmax(scale * Q K^T [+ causal mask]) V and
+ * LSE_i = m_i + ln(l_i) (Symbol Map; "Putting It Together", epilogue row: O is divided by
+ * l and only O and L are written). O and LSE are overwritten. */
+attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int N, int d, int causal, float scale,
+                       attn_dtype_t dtype, attn_stream_t stream);
+
+/* Bytes of device workspace attn_bwd needs: fp32 D = rowsum(dO o O), [B][H][N]. */
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/* Backward pass with LSE recomputation (Deep Dive "Backward warp specialization": S and P
+ * are recomputed from L, then dP, dS, dV, dK and dQ are formed). Inputs are the forward's
+ * Q, K, V, O, LSE and the output gradient dO; dQ, dK, dV are overwritten (not accumulated).
+ * `workspace` must hold attn_bwd_workspace_bytes(B,H,N,d) bytes; its contents on entry
+ * are ignored and on return unspecified. The result is deterministic (no atomics). */
+attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                       int B, int H, int N, int d, int causal, float scale,
+                       attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                       attn_stream_t stream);
+
+/* FP8 block quantisation ("FP8 accuracy controls": one fp32 scale per block; incoherent
+ * processing multiplies Q and K by the same orthogonal M = diag(s) H_d / sqrt(d)).
+ * x [B][N][H][d] (dtype) -> x8 e4m3 codes and descale [B][H][ceil(N/64)].
+ * rotate != 0 applies M with signs s_t = (top bit of SplitMix64 output t for
+ * `hadamard_seed`) ? -1 : +1; rotate = 0 quantises x as is (use it for V).
+ * descale = fp32(amax/448) of the rotated block (1 for an all-zero block); codes are
+ * round-to-nearest-even of value/descale, saturated to +-448. */
+attn_status_t attn_fp8_quantize(const void* x, uint8_t* x8, float* descale,
+                                int B, int H, int N, int d, attn_dtype_t dtype,
+                                int rotate, uint64_t hadamard_seed, attn_stream_t stream);
+
+/* FP8 forward attention ("FP8 layout conformance", "FP8 accuracy controls"):
+ * O = softmax(scale * Qh Kh^T [+ mask]) Vh with Xh = e4m3(X8) * descale_X per 64-row block.
+ * Q8 and K8 must have been rotated with the same seed (or both not at all); because the
+ * rotation is orthogonal the scores do not depend on it, and `hadamard_seed` is carried
+ * only to describe the inputs. The probabilities are rounded to e4m3 (scaled by 2^8) for
+ * the P V product. O is written in `out_dtype`, LSE in fp32 (natural log). */
+attn_status_t attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                           void* o, float* lse, int B, int H, int N, int d, int causal,
+                           float scale, const float* descale_q, const float* descale_k,
+                           const float* descale_v, uint64_t hadamard_seed,
+                           attn_dtype_t out_dtype, attn_stream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* attn_strerror(attn_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ATTN_H */
