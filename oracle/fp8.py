@@ -18,7 +18,8 @@ Readings where the pages are silent or disagree:
     (the "natural attention tiles" of the explainer; a split of d would break the single
     contraction over d).
   * descale = fp32(fp32(amax) / 448), and descale = 1 when amax = 0; the stored code is
-    RNE(y / descale), the dequantised value is decode(code) * descale.
+    RNE of the fp32 quotient fp32(fp32(y) / descale) (the scale arithmetic is fp32, so the
+    code is decided on that fp32 value); the dequantised value is decode(code) * descale.
   * M = diag(s) H_d / sqrt(d), H_d the Sylvester Hadamard matrix, one sign vector s per
     call shared by every (batch, head) and by Q and K; s_t = +1 unless the top bit of the
     t-th SplitMix64 output for `seed` is set (then -1). V is never rotated.
@@ -129,7 +130,8 @@ def quantize_blocks(x, rotate, seed=0, block=FP8_BLOCK_ROWS):
                 amax = np.float32(np.abs(tile).max())
                 ds = np.float32(amax / np.float32(E4M3_MAX)) if amax > 0 else np.float32(1.0)
                 descale[b, h, j] = ds
-                codes[b, j * block:(j + 1) * block, h] = e4m3_encode(tile / np.float64(ds))
+                scaled = tile.astype(np.float32) / ds          # fp32 / fp32, correctly rounded
+                codes[b, j * block:(j + 1) * block, h] = e4m3_encode(scaled.astype(np.float64))
     return codes, descale, y
 
 
