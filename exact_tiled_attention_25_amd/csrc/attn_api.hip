@@ -48,6 +48,14 @@ attn_status_t launched(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E
 
 constexpr double kLog2e = 1.4426950408889634074;
 
+// SplitMix64 (Steele, Lea and Flood, 2014): output t of the generator seeded with `seed`.
+uint64_t splitmix64_output(uint64_t seed, uint64_t t) {
+  uint64_t z = seed + (t + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
 }  // namespace
 
 extern "C" {
@@ -101,7 +109,10 @@ attn_status_t attn_fp8_quantize(const void* x, uint8_t* x8, float* descale,
   if (st != ATTN_OK || empty) return st;
   if (!x || !x8 || !descale) return ATTN_EINVAL;
   if ((st = check_device()) != ATTN_OK) return st;
-  attn::Fp8QuantParams p{x, x8, descale, B, H, N, rotate != 0, hadamard_seed};
+  attn::Fp8QuantParams p{x, x8, descale, B, H, N, rotate != 0, {0, 0, 0, 0, 0, 0, 0, 0}};
+  if (rotate)
+    for (int t = 0; t < d; ++t)
+      if (splitmix64_output(hadamard_seed, (uint64_t)t) >> 63) p.neg[t >> 5] |= 1u << (t & 31);
   (void)hipGetLastError();
   return launched(attn::launch_fp8_quantize(dtype == ATTN_BF16, d, p, (hipStream_t)stream));
 }

@@ -37,7 +37,7 @@ struct Fp8QuantParams {
   float* descale;
   int B, H, N;
   int rotate;
-  uint64_t seed;
+  uint32_t neg[8];  // bit t set: dim t of the random sign vector is -1 (d <= 256)
 };
 
 struct Fp8FwdParams {
