@@ -36,7 +36,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=1, help="heads of the workload timed on the oracle")
+    ap.add_argument("--cpu-heads", type=int, default=8, help="heads of the workload timed on the oracle")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (HBM counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
 
 
@@ -138,6 +140,14 @@ def main():
             ev[n][i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     comp_out = {}
     for n, (fn, flops, nbytes, pk) in active.items():
