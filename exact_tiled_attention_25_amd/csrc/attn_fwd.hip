@@ -55,7 +55,7 @@ __device__ __forceinline__ int vswz(int d) {
 }
 
 template <bool BF16, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   constexpr int BC = FwdCfg<D>::BC;
   constexpr int KP = D * 2 + 16;         // K tile row pitch (bytes), padded against bank conflicts
   constexpr int KBYTES = BC * KP;
