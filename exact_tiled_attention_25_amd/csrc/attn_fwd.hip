@@ -40,7 +40,7 @@ namespace {
 
 template <int D> struct FwdCfg;
 // BC: keys per tile; OCC: waves per SIMD the register budget is sized for.
-template <> struct FwdCfg<64> { static constexpr int BC = 128, OCC = 2; };
+template <> struct FwdCfg<64> { static constexpr int BC = 64, OCC = 2; };
 template <> struct FwdCfg<128> { static constexpr int BC = 64, OCC = 2; };
 template <> struct FwdCfg<256> { static constexpr int BC = 64, OCC = 1; };
 
@@ -50,16 +50,84 @@ constexpr int kBR = kWaves * kQW;        // query rows per workgroup
 constexpr float kTau = 8.0f;             // lazy-rescale threshold (log2 units)
 constexpr float kLn2 = 0.69314718055994530942f;
 
+// Scores of one key tile for this wave: s[kb] = K[kb*32 .. +31] Q^T (32 keys x 32 queries).
+template <bool BF16, int D, int NKB>
+__device__ __forceinline__ void tile_scores(f32x16 (&s)[NKB], const char* ks, const u32x4 (&qreg)[D / 16], int l32, int hf) {
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    s[kb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) s[kb] = mfma32x16<BF16>(lds_row<D>(ks, kb * 32 + l32, kk, hf), qreg[kk], s[kb]);
+  }
+}
+
+// Causal / ragged mask of a tile: keys past N or past the query become -inf.
+template <bool CAUSAL, int NKB>
+__device__ __forceinline__ void tile_mask(f32x16 (&s)[NKB], int k0, int N, int qrow, int hf) {
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+      if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
+    }
+}
+
+// Row maximum (in the exp2 domain) of a tile; -inf if every key of the row is masked.
+template <int NKB>
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[NKB], float c) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+  mx = xhalf_max(mx);
+  return mx == -INFINITY ? -INFINITY : mx * c;
+}
+
+// P~ = exp2(s*c - m) packed to 16-bit MFMA B operands (16 keys per operand); returns the
+// lane's partial row sum of the fp32 P~.
+template <bool BF16, bool EDGE, int NKB>
+__device__ __forceinline__ float tile_exp(const f32x16 (&s)[NKB], u32x4 (&pk)[2 * NKB], float c, float m_use) {
+  float psum = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      float e[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float x = s[kb][8 * h2 + t];
+        e[t] = fast_exp2(fmaf(x, c, -m_use));
+        if constexpr (EDGE) e[t] = (x == -INFINITY) ? 0.f : e[t];
+        psum += e[t];
+      }
+      pk[2 * kb + h2] = u32x4{pack2<BF16>(e[0], e[1]), pack2<BF16>(e[2], e[3]), pack2<BF16>(e[4], e[5]),
+                              pack2<BF16>(e[6], e[7])};
+    }
+  return psum;
+}
+
+// O^T += V^T P^T for one tile (V row-major in LDS, gathered by transpose reads).
+template <bool BF16, int D, int NKB>
+__device__ __forceinline__ void tile_pv(f32x16 (&oacc)[D / 32], const char* vs, const u32x4 (&pk)[2 * NKB], int lane) {
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+    for (int cidx = 0; cidx < 2 * NKB; ++cidx)
+      oacc[i] = mfma32x16<BF16>(lds_tr<D>(vs, 16 * cidx, 32 * i, lane), pk[cidx], oacc[i]);
+}
+
 template <bool BF16, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
   constexpr int BC = FwdCfg<D>::BC;
   constexpr int TB = BC * 2 * D;         // bytes of one K or V tile
-  constexpr int STAGE = 2 * TB;
   constexpr int NKB = BC / 32;
   constexpr int NDB = D / 32;
   constexpr int NKS = D / 16;
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  // K ring (2 stages, fetched two tiles ahead) then V ring (2 stages, one tile ahead).
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -72,6 +140,7 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
   const int h = bh % H, b = bh / H;
   const int qt = CAUSAL ? nqt - 1 - qi : qi;
   const int q0 = qt * kBR + wave * kQW;
+  const int qrow = q0 + l32;
 
   // Per-(batch, head) buffer views: offset = row * row_bytes + byte within the head's row.
   const uint32_t row_bytes = (uint32_t)H * D * 2;
@@ -84,106 +153,153 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
 
   const int kend = CAUSAL ? min(N, (qt + 1) * kBR) : N;
   const int nkt = (kend + BC - 1) / BC;
-  auto fetch = [&](int k0, int stage) {
-    char* st = smem + stage * STAGE;
-    dma_tile<D, BC, false, kWaves>(st, rk, k0, row_bytes, wave, lane);
-    dma_tile<D, BC, true, kWaves>(st + TB, rv, k0, row_bytes, wave, lane);
-  };
-  fetch(0, 0);
+  // tiles this wave computes: causal rows stop at the diagonal tile; rows past N compute none
+  const int nkt_w = q0 >= N ? 0 : CAUSAL ? min(nkt, (q0 + kQW - 1) / BC + 1) : nkt;
+  auto kst = [&](int j) { return smem + (j & 1) * TB; };
+  auto vst = [&](int j) { return smem + (2 + (j & 1)) * TB; };
+  auto is_edge = [&](int j) { const int k0 = j * BC; return (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0); };
+
+  dma_tile<D, BC, false, kWaves>(kst(0), rk, 0, row_bytes, wave, lane);
+  dma_tile<D, BC, true, kWaves>(vst(0), rv, 0, row_bytes, wave, lane);
+  if (nkt > 1) dma_tile<D, BC, false, kWaves>(kst(1), rk, BC, row_bytes, wave, lane);
 
   // Q^T operand: lane holds query q0 + l32, dims 16*ks + 8*hf .. +7.
   u32x4 qreg[NKS];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) qreg[ks] = buf_load16(rq, (uint32_t)(q0 + l32) * row_bytes + (16 * ks + 8 * hf) * 2);
+  for (int ks = 0; ks < NKS; ++ks) qreg[ks] = buf_load16(rq, (uint32_t)qrow * row_bytes + (16 * ks + 8 * hf) * 2);
 
   f32x16 oacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
-  const bool wave_live = q0 < N;
-  const int qrow = q0 + l32;
   const float c = p.c;
 
   wait_dma();
   __syncthreads();
 
-  for (int j = 0; j < nkt; ++j) {
-    const int k0 = j * BC;
-    if (j + 1 < nkt) fetch(k0 + BC, (j + 1) & 1);
-    const char* ks = smem + (j & 1) * STAGE;
-    const char* vs = ks + TB;
-    const bool skip = !wave_live || (CAUSAL && k0 > q0 + kQW - 1);
-    auto tile = [&](auto edge_tag) {
-      constexpr bool EDGE = decltype(edge_tag)::value;
-      f32x16 s[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        s[kb] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < NKS; ++kk) s[kb] = mfma32x16<BF16>(lds_row<D>(ks, kb * 32 + l32, kk, hf), qreg[kk], s[kb]);
-      }
-      if constexpr (EDGE) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = xhalf_max(mx);
-      float mt = mx * c;
-      if constexpr (EDGE) mt = (mx == -INFINITY) ? -INFINITY : mt;
-      const float m_cand = fmaxf(m_run, mt);
-      if (__builtin_amdgcn_ballot_w64(m_cand > m_run + kTau)) {
-        const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_cand);
-        m_run = m_cand;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < NDB; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      float psum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float e = fast_exp2(fmaf(s[kb][r], c, -m_use));
-          if constexpr (EDGE) e = (s[kb][r] == -INFINITY) ? 0.f : e;
-          s[kb][r] = e;
-          psum += e;
-        }
-      l_run += psum;
-      u32x4 pk[BC / 16];
-#pragma unroll
-      for (int cidx = 0; cidx < BC / 16; ++cidx) {
-        const int kb = cidx >> 1, base = (cidx & 1) * 8;
-        pk[cidx] = u32x4{pack2<BF16>(s[kb][base + 0], s[kb][base + 1]), pack2<BF16>(s[kb][base + 2], s[kb][base + 3]),
-                         pack2<BF16>(s[kb][base + 4], s[kb][base + 5]), pack2<BF16>(s[kb][base + 6], s[kb][base + 7])};
-      }
+  // Two-stage software pipeline (per wave): while the scores of tile j+1 are being
+  // multiplied out on the MFMA pipe, the VALU exponentiates tile j; while P~(j) V(j) runs,
+  // the VALU takes the row maximum of tile j+1.
+  f32x16 sc[NKB], sn[NKB];
+  float mx_next = -INFINITY;
+  if (nkt_w > 0) {
+    tile_scores<BF16, D, NKB>(sc, kst(0), qreg, l32, hf);
+    if (is_edge(0)) tile_mask<CAUSAL, NKB>(sc, 0, N, qrow, hf);
+    mx_next = tile_max<NKB>(sc, c);
+  }
+
+  auto prefetch = [&](int j) {
+    if (j + 1 < nkt) dma_tile<D, BC, true, kWaves>(vst(j + 1), rv, (j + 1) * BC, row_bytes, wave, lane);
+    if (j + 2 < nkt) dma_tile<D, BC, false, kWaves>(kst(j + 2), rk, (j + 2) * BC, row_bytes, wave, lane);
+  };
+  // the maximum of tile j (taken one step earlier) may move the reference: rescale O and l
+  auto rescale = [&]() {
+    const float m_cand = fmaxf(m_run, mx_next);
+    if (__builtin_amdgcn_ballot_w64(m_cand > m_run + kTau)) {
+      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_cand);
+      m_run = m_cand;
+      l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < NDB; ++i)
 #pragma unroll
-        for (int cidx = 0; cidx < BC / 16; ++cidx)
-          oacc[i] = mfma32x16<BF16>(lds_tr<D>(vs, 16 * cidx, 32 * i, lane), pk[cidx], oacc[i]);
-    };
-    if (!skip) {
-      const bool edge = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0);
-      if (edge) tile(std::true_type{});
-      else tile(std::false_type{});
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+    }
+  };
+
+  // Interior tiles (neither tile j nor j+1 masked; masking only ever starts near the end of
+  // a wave's key range): the pipelined form, with the instruction order written out.
+  // Block 1 issues one S(j+1) MFMA per step and, under it, exponentiates two scores of
+  // tile j; block 2 issues one P~(j)V(j) MFMA per step with one max3 of tile j+1 under it.
+  // LDS operands are fetched PF steps ahead; sched_barrier fences keep each step's order.
+  constexpr int S1 = NKB * NKS;       // MFMAs in block 1
+  constexpr int S2 = NDB * 2 * NKB;   // MFMAs in block 2
+  constexpr int EPS = 16 * NKB / S1;  // scores exponentiated per block-1 step (256/d)
+  constexpr int MPS = 16 * NKB / S2;  // scores folded into the max per block-2 step (512/d)
+  constexpr int PF = 3;
+  static_assert(EPS * S1 == 16 * NKB && MPS * S2 == 16 * NKB && EPS >= 1 && MPS >= 1, "step split");
+  auto fast_iter = [&](int jj, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) {
+    prefetch(jj);
+    rescale();
+    const float m_use = m_run;
+    const char* kn = kst(jj + 1);
+    const char* vc = vst(jj);
+    u32x4 pk[2 * NKB];
+    u32x4 kop[S1];
+    float e[16 * NKB];
+    float psum = 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < PF; ++t) kop[t] = lds_row<D>(kn, (t / NKS) * 32 + l32, t % NKS, hf);
+#pragma unroll
+    for (int t = 0; t < S1; ++t) {
+      if (t + PF < S1) kop[t + PF] = lds_row<D>(kn, ((t + PF) / NKS) * 32 + l32, (t + PF) % NKS, hf);
+      const int kb = t / NKS, kk = t % NKS;
+      nxt[kb] = mfma32x16<BF16>(kop[t], qreg[kk], kk == 0 ? f32x16{} : nxt[kb]);
+#pragma unroll
+      for (int u = 0; u < EPS; ++u) {
+        const int i = EPS * t + u;
+        e[i] = fast_exp2(fmaf(cur[i >> 4][i & 15], c, -m_use));
+        psum += e[i];
+      }
+      if ((EPS * (t + 1)) % 8 == 0) {
+        const int q = EPS * (t + 1) / 8 - 1;   // 8 scores -> one 16-key operand
+        pk[q] = u32x4{pack2<BF16>(e[8 * q + 0], e[8 * q + 1]), pack2<BF16>(e[8 * q + 2], e[8 * q + 3]),
+                      pack2<BF16>(e[8 * q + 4], e[8 * q + 5]), pack2<BF16>(e[8 * q + 6], e[8 * q + 7])};
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += psum;
+    u32x4 vop[S2];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < PF; ++t) vop[t] = lds_tr<D>(vc, 16 * (t % (2 * NKB)), 32 * (t / (2 * NKB)), lane);
+#pragma unroll
+    for (int t = 0; t < S2; ++t) {
+      if (t + PF < S2) vop[t + PF] = lds_tr<D>(vc, 16 * ((t + PF) % (2 * NKB)), 32 * ((t + PF) / (2 * NKB)), lane);
+      const int i = t / (2 * NKB), cidx = t % (2 * NKB);
+      oacc[i] = mfma32x16<BF16>(vop[t], pk[cidx], oacc[i]);
+      // the row max of tile j+1, MPS scores per step
+#pragma unroll
+      for (int u = 0; u < MPS; ++u) {
+        const int i = MPS * t + u;
+        mx = fmaxf(mx, nxt[i >> 4][i & 15]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mx = xhalf_max(mx);
+    mx_next = mx * c;
+    wait_dma();
+    __syncthreads();
+  };
+  int j = 0;
+  for (; j + 1 < nkt_w && !is_edge(j + 1);) {
+    fast_iter(j, sc, sn);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sc[kb] = sn[kb];
+    ++j;
+  }
+  // Remaining tiles, in order: masked tiles and the tail of the key range (and, for waves
+  // with nothing left to compute, only the ring bookkeeping every wave takes part in).
+  for (; j < nkt; ++j) {
+    prefetch(j);
+    if (j < nkt_w) {
+      rescale();
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      u32x4 pk[2 * NKB];
+      if (is_edge(j)) l_run += tile_exp<BF16, true, NKB>(sc, pk, c, m_use);
+      else l_run += tile_exp<BF16, false, NKB>(sc, pk, c, m_use);
+      tile_pv<BF16, D, NKB>(oacc, vst(j), pk, lane);
+      if (j + 1 < nkt_w) {
+        tile_scores<BF16, D, NKB>(sc, kst(j + 1), qreg, l32, hf);
+        if (is_edge(j + 1)) tile_mask<CAUSAL, NKB>(sc, (j + 1) * BC, N, qrow, hf);
+        mx_next = tile_max<NKB>(sc, c);
+      }
     }
     wait_dma();
     __syncthreads();
   }
 
-  if (wave_live) {
+  if (nkt_w > 0) {
     const float l_tot = xhalf_sum(l_run);
     const float inv = 1.0f / l_tot;
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;

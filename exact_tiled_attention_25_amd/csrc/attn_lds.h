@@ -15,7 +15,11 @@
 //    element i%4 of the 8-byte pieces that source lanes 4j + i/4 (j = 0..3) point at.
 //    Pointing source lane s at row (base + s/4) and dims (d0 + 4*(s%4)) hands lane i the
 //    column d0 + i of four consecutive rows: an MFMA operand whose contraction runs over
-//    rows, read from a row-major tile. swz_tr(r) = 2*(r & 3) spreads the 4 rows of a group.
+//    rows, read from a row-major tile. A 16-lane group reads 2 chunks of each of 4 rows and
+//    the two groups of a half-wave read the next 2 chunks of the same rows; swz_tr(r) =
+//    (2j ^ 4j) & 15 (j = r & 3) gives the 4 rows disjoint bank sets both within a group
+//    (bits 1-2 distinct) and across the half-wave (bits 2-3 distinct); for d = 64 the
+//    128-byte rows already alternate bank halves and 2j suffices.
 #pragma once
 #include "attn_device.h"
 
@@ -29,12 +33,17 @@ __device__ __forceinline__ int swz_row(int r) {
   if constexpr (D == 64) return (r ^ (r >> 3)) & 7;
   else return r & 15;
 }
-__device__ __forceinline__ int swz_tr(int r) { return 2 * (r & 3); }
+template <int D>
+__device__ __forceinline__ int swz_tr(int r) {
+  const int j = r & 3;
+  if constexpr (D == 64) return 2 * j;
+  else return ((2 * j) ^ (4 * j)) & 15;
+}
 
 // Byte offset of the 16-byte chunk holding dims [8c, 8c+8) of row r.
 template <int D, bool TR>
 __device__ __forceinline__ int chunk_off(int r, int c) {
-  return r * (2 * D) + ((c ^ (TR ? swz_tr(r) : swz_row<D>(r))) << 4);
+  return r * (2 * D) + ((c ^ (TR ? swz_tr<D>(r) : swz_row<D>(r))) << 4);
 }
 
 // DMA one ROWS x D tile (rows row0 .. row0+ROWS-1 of the buffer view) into `dst`.
@@ -52,7 +61,7 @@ __device__ __forceinline__ void dma_tile(char* dst, __amdgpu_buffer_rsrc_t rs, i
     const int byte = blk * 1024 + 16 * lane;
     const int r = byte / (2 * D);
     const int cp = (byte % (2 * D)) >> 4;
-    const int c = (cp ^ (TR ? swz_tr(r) : swz_row<D>(r))) & (NCH - 1);
+    const int c = (cp ^ (TR ? swz_tr<D>(r) : swz_row<D>(r))) & (NCH - 1);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + blk * 1024), 16,
                                              (uint32_t)(row0 + r) * row_bytes + c * 16, 0, 0, 0);
   }
