@@ -20,7 +20,10 @@ ARCH = "gfx950"
 
 # -packed-fp32-ops: never emit v_pk_{add,mul,fma}_f32 (hipcc's host pass warns that it does
 # not know the feature; that warning is harmless).
-FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+# -fno-honor-nans: no kernel input or intermediate is NaN by construction (masked scores are
+# -inf, which stays honoured), and it lets fmax chains fuse into v_max3_f32 without the
+# operand canonicalisation that IEEE mode otherwise inserts.
+FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-fno-honor-nans",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          f"-I{os.path.join(ROOT, 'include')}"]
 
@@ -43,6 +46,14 @@ def build(verbose=False, jobs=None):
         outs = list(ex.map(lambda so: _run([HIPCC, *FLAGS, "-c", so[0], "-o", so[1]]), zip(srcs, objs)))
     tmp = LIB + ".tmp"
     outs.append(_run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]))
+    # The host compilation pass can silently drop a kernel's launch stub (for instance when
+    # substitution fails in device-only code); the library would then fail to load. Catch
+    # that here rather than at first use.
+    und = subprocess.run(["nm", "-C", "--undefined-only", tmp], stdout=subprocess.PIPE, text=True).stdout
+    missing = [l.strip() for l in und.splitlines() if "__device_stub__" in l]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("kernel launch stubs missing from the host objects:\n" + "\n".join(missing))
     os.replace(tmp, LIB)
     if verbose:
         for o in outs:

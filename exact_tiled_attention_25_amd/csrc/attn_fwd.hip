@@ -52,12 +52,12 @@ constexpr float kLn2 = 0.69314718055994530942f;
 
 // Scores of one key tile for this wave: s[kb] = K[kb*32 .. +31] Q^T (32 keys x 32 queries).
 template <bool BF16, int D, int NKB>
-__device__ __forceinline__ void tile_scores(f32x16 (&s)[NKB], const char* ks, const u32x4 (&qreg)[D / 16], int l32, int hf) {
+__device__ __forceinline__ void tile_scores(f32x16 (&s)[NKB], const char* kl, const u32x4 (&qreg)[D / 16]) {
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     s[kb] = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) s[kb] = mfma32x16<BF16>(lds_row<D>(ks, kb * 32 + l32, kk, hf), qreg[kk], s[kb]);
+    for (int kk = 0; kk < D / 16; ++kk) s[kb] = mfma32x16<BF16>(lds_k<D>(kl, kb, kk), qreg[kk], s[kb]);
   }
 }
 
@@ -110,24 +110,25 @@ __device__ __forceinline__ float tile_exp(const f32x16 (&s)[NKB], u32x4 (&pk)[2 
 
 // O^T += V^T P^T for one tile (V row-major in LDS, gathered by transpose reads).
 template <bool BF16, int D, int NKB>
-__device__ __forceinline__ void tile_pv(f32x16 (&oacc)[D / 32], const char* vs, const u32x4 (&pk)[2 * NKB], int lane) {
+__device__ __forceinline__ void tile_pv(f32x16 (&oacc)[D / 32], const char* vl, const u32x4 (&pk)[2 * NKB]) {
 #pragma unroll
   for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-    for (int cidx = 0; cidx < 2 * NKB; ++cidx)
-      oacc[i] = mfma32x16<BF16>(lds_tr<D>(vs, 16 * cidx, 32 * i, lane), pk[cidx], oacc[i]);
+    for (int cidx = 0; cidx < 2 * NKB; ++cidx) oacc[i] = mfma32x16<BF16>(lds_vt<D>(vl, cidx, i), pk[cidx], oacc[i]);
 }
 
 template <bool BF16, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
   constexpr int BC = FwdCfg<D>::BC;
-  constexpr int TB = BC * 2 * D;         // bytes of one K or V tile
   constexpr int NKB = BC / 32;
   constexpr int NDB = D / 32;
   constexpr int NKS = D / 16;
+  using KPlan = DmaPlan<D, BC, k_pitch<D>(), kWaves>;
+  using VPlan = DmaPlan<D, BC, v_pitch<D>(), kWaves>;
 
   // K ring (2 stages, fetched two tiles ahead) then V ring (2 stages, one tile ahead).
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TB];
+  constexpr int KBYTES = BC * k_pitch<D>(), VBYTES = BC * v_pitch<D>();
+  __shared__ __attribute__((aligned(1024))) char smem[2 * KBYTES + 2 * VBYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -147,21 +148,24 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
   const size_t head_off = ((size_t)b * N * H + h) * D * 2;
   const uint32_t nrec = (uint32_t)N * row_bytes - (uint32_t)h * D * 2;
   const auto rq = make_rsrc((const char*)p.q + head_off, nrec);
-  const auto rk = make_rsrc((const char*)p.k + head_off, nrec);
-  const auto rv = make_rsrc((const char*)p.v + head_off, nrec);
   const auto ro = make_rsrc((const char*)p.o + head_off, nrec);
 
   const int kend = CAUSAL ? min(N, (qt + 1) * kBR) : N;
   const int nkt = (kend + BC - 1) / BC;
   // tiles this wave computes: causal rows stop at the diagonal tile; rows past N compute none
   const int nkt_w = q0 >= N ? 0 : CAUSAL ? min(nkt, (q0 + kQW - 1) / BC + 1) : nkt;
-  auto kst = [&](int j) { return smem + (j & 1) * TB; };
-  auto vst = [&](int j) { return smem + (2 + (j & 1)) * TB; };
+  auto kst = [&](int j) { return smem + (j & 1) * KBYTES; };
+  auto vst = [&](int j) { return smem + 2 * KBYTES + (j & 1) * VBYTES; };
+  const int k_lane = k_lane_off<D>(lane), v_lane = v_lane_off<D>(lane);
   auto is_edge = [&](int j) { const int k0 = j * BC; return (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0); };
-
-  dma_tile<D, BC, false, kWaves>(kst(0), rk, 0, row_bytes, wave, lane);
-  dma_tile<D, BC, true, kWaves>(vst(0), rv, 0, row_bytes, wave, lane);
-  if (nkt > 1) dma_tile<D, BC, false, kWaves>(kst(1), rk, BC, row_bytes, wave, lane);
+  uint32_t kvoff[KPlan::NPW], vvoff[VPlan::NPW];
+  dma_init<KPlan, kWaves>(kvoff, row_bytes, wave, lane);
+  dma_init<VPlan, kWaves>(vvoff, row_bytes, wave, lane);
+  const char* kbase = (const char*)p.k + head_off;
+  const char* vbase = (const char*)p.v + head_off;
+  dma_issue<KPlan, kWaves>(kvoff, kst(0), kbase, 0, row_bytes, nrec, wave);
+  dma_issue<VPlan, kWaves>(vvoff, vst(0), vbase, 0, row_bytes, nrec, wave);
+  if (nkt > 1) dma_issue<KPlan, kWaves>(kvoff, kst(1), kbase, BC, row_bytes, nrec, wave);
 
   // Q^T operand: lane holds query q0 + l32, dims 16*ks + 8*hf .. +7.
   u32x4 qreg[NKS];
@@ -183,14 +187,14 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
   f32x16 sc[NKB], sn[NKB];
   float mx_next = -INFINITY;
   if (nkt_w > 0) {
-    tile_scores<BF16, D, NKB>(sc, kst(0), qreg, l32, hf);
+    tile_scores<BF16, D, NKB>(sc, kst(0) + k_lane, qreg);
     if (is_edge(0)) tile_mask<CAUSAL, NKB>(sc, 0, N, qrow, hf);
     mx_next = tile_max<NKB>(sc, c);
   }
 
   auto prefetch = [&](int j) {
-    if (j + 1 < nkt) dma_tile<D, BC, true, kWaves>(vst(j + 1), rv, (j + 1) * BC, row_bytes, wave, lane);
-    if (j + 2 < nkt) dma_tile<D, BC, false, kWaves>(kst(j + 2), rk, (j + 2) * BC, row_bytes, wave, lane);
+    if (j + 1 < nkt) dma_issue<VPlan, kWaves>(vvoff, vst(j + 1), vbase, (j + 1) * BC, row_bytes, nrec, wave);
+    if (j + 2 < nkt) dma_issue<KPlan, kWaves>(kvoff, kst(j + 2), kbase, (j + 2) * BC, row_bytes, nrec, wave);
   };
   // the maximum of tile j (taken one step earlier) may move the reference: rescale O and l
   auto rescale = [&]() {
@@ -221,18 +225,18 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
     prefetch(jj);
     rescale();
     const float m_use = m_run;
-    const char* kn = kst(jj + 1);
-    const char* vc = vst(jj);
+    const char* kn = kst(jj + 1) + k_lane;
+    const char* vc = vst(jj) + v_lane;
     u32x4 pk[2 * NKB];
     u32x4 kop[S1];
     float e[16 * NKB];
     float psum = 0.f;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < PF; ++t) kop[t] = lds_row<D>(kn, (t / NKS) * 32 + l32, t % NKS, hf);
+    for (int t = 0; t < PF; ++t) kop[t] = lds_k<D>(kn, t / NKS, t % NKS);
 #pragma unroll
     for (int t = 0; t < S1; ++t) {
-      if (t + PF < S1) kop[t + PF] = lds_row<D>(kn, ((t + PF) / NKS) * 32 + l32, (t + PF) % NKS, hf);
+      if (t + PF < S1) kop[t + PF] = lds_k<D>(kn, (t + PF) / NKS, (t + PF) % NKS);
       const int kb = t / NKS, kk = t % NKS;
       nxt[kb] = mfma32x16<BF16>(kop[t], qreg[kk], kk == 0 ? f32x16{} : nxt[kb]);
 #pragma unroll
@@ -252,17 +256,21 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
     u32x4 vop[S2];
     float mx = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < PF; ++t) vop[t] = lds_tr<D>(vc, 16 * (t % (2 * NKB)), 32 * (t / (2 * NKB)), lane);
+    for (int t = 0; t < PF; ++t) vop[t] = lds_vt<D>(vc, t % (2 * NKB), t / (2 * NKB));
 #pragma unroll
     for (int t = 0; t < S2; ++t) {
-      if (t + PF < S2) vop[t + PF] = lds_tr<D>(vc, 16 * ((t + PF) % (2 * NKB)), 32 * ((t + PF) / (2 * NKB)), lane);
+      if (t + PF < S2) vop[t + PF] = lds_vt<D>(vc, (t + PF) % (2 * NKB), (t + PF) / (2 * NKB));
       const int i = t / (2 * NKB), cidx = t % (2 * NKB);
       oacc[i] = mfma32x16<BF16>(vop[t], pk[cidx], oacc[i]);
       // the row max of tile j+1, MPS scores per step
+      if constexpr (MPS == 1) {
+        mx = fmaxf(mx, nxt[t >> 4][t & 15]);
+      } else {
 #pragma unroll
-      for (int u = 0; u < MPS; ++u) {
-        const int i = MPS * t + u;
-        mx = fmaxf(mx, nxt[i >> 4][i & 15]);
+        for (int u = 0; u < MPS; u += 2) {
+          const int i = MPS * t + u;
+          mx = fmaxf(mx, fmaxf(nxt[i >> 4][i & 15], nxt[(i + 1) >> 4][(i + 1) & 15]));
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -272,7 +280,11 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
     __syncthreads();
   };
   int j = 0;
-  for (; j + 1 < nkt_w && !is_edge(j + 1);) {
+  for (; j + 2 < nkt_w && !is_edge(j + 2); j += 2) {   // sc/sn swap roles: no copies
+    fast_iter(j, sc, sn);
+    fast_iter(j + 1, sn, sc);
+  }
+  if (j + 1 < nkt_w && !is_edge(j + 1)) {
     fast_iter(j, sc, sn);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) sc[kb] = sn[kb];
@@ -288,9 +300,9 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
       u32x4 pk[2 * NKB];
       if (is_edge(j)) l_run += tile_exp<BF16, true, NKB>(sc, pk, c, m_use);
       else l_run += tile_exp<BF16, false, NKB>(sc, pk, c, m_use);
-      tile_pv<BF16, D, NKB>(oacc, vst(j), pk, lane);
+      tile_pv<BF16, D, NKB>(oacc, vst(j) + v_lane, pk);
       if (j + 1 < nkt_w) {
-        tile_scores<BF16, D, NKB>(sc, kst(j + 1), qreg, l32, hf);
+        tile_scores<BF16, D, NKB>(sc, kst(j + 1) + k_lane, qreg);
         if (is_edge(j + 1)) tile_mask<CAUSAL, NKB>(sc, (j + 1) * BC, N, qrow, hf);
         mx_next = tile_max<NKB>(sc, c);
       }

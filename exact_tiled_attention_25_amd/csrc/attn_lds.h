@@ -1,25 +1,23 @@
 // LDS tiles filled by direct HBM->LDS DMA (buffer_load_dwordx4 ... lds) and read as MFMA
 // operands, for 16-bit tiles of ROWS tokens x D dims of one (batch, head).
 //
-// DMA: one wave instruction writes 1 KiB of LDS, lane l's 16 bytes at (M0 base + 16*l); the
-// global address of each lane is free. The tile is stored row-major without padding (row
-// pitch 2*D bytes); bank conflicts are avoided by XOR-swizzling the 16-byte chunk index of
-// each row: LDS chunk c' of row r holds global chunk c = c' ^ swz(r). Rows past the end of
-// the sequence arrive as zeros through the buffer range check.
+// Layout: row-major with padded row pitches, so that every operand read is a per-lane base
+// address plus a compile-time offset (no per-read address arithmetic):
+//  * K tiles, pitch 2D + 16 bytes: a 16-lane group reading 16 bytes of 16 consecutive rows
+//    at the same column hits 16 disjoint 4-bank sets (pitch = 4 banks mod 64).
+//  * V tiles, pitch 2D + 64 bytes: read with ds_read_b64_tr_b16. Within each 16-lane group,
+//    lane i receives element i%4 of the 8-byte pieces that source lanes 4j + i/4 (j = 0..3)
+//    point at; pointing source lane s at row (base + s/4), dims (d0 + 4*(s%4)) hands lane i
+//    dim d0 + i of four consecutive rows - an MFMA operand whose contraction runs over rows.
+//    A 32-lane half-wave then covers 4 rows x 64 bytes, and a pitch of 16 banks mod 64 puts
+//    the 4 rows on disjoint bank sets (the LDS has 64 banks of 4 bytes).
 //
-// Two read patterns, each with its own swizzle:
-//  * row reads (ds_read_b128): lane l reads 16 bytes of row `r` (rows of a 32-row block go
-//    to lanes l%32). swz_row(r) = (r ^ (r >> 3)) & 7 for D = 64, r & 15 otherwise, so any 8
-//    or 16 consecutive rows hit distinct banks.
-//  * transposed reads (ds_read_b64_tr_b16): within each 16-lane group, lane i receives
-//    element i%4 of the 8-byte pieces that source lanes 4j + i/4 (j = 0..3) point at.
-//    Pointing source lane s at row (base + s/4) and dims (d0 + 4*(s%4)) hands lane i the
-//    column d0 + i of four consecutive rows: an MFMA operand whose contraction runs over
-//    rows, read from a row-major tile. A 16-lane group reads 2 chunks of each of 4 rows and
-//    the two groups of a half-wave read the next 2 chunks of the same rows; swz_tr(r) =
-//    (2j ^ 4j) & 15 (j = r & 3) gives the 4 rows disjoint bank sets both within a group
-//    (bits 1-2 distinct) and across the half-wave (bits 2-3 distinct); for d = 64 the
-//    128-byte rows already alternate bank halves and 2j suffices.
+// DMA: one wave instruction writes 1 KiB of LDS, lane l's 16 bytes at (M0 base + 16*l); the
+// global address of each lane is free. With padded rows, lane slots that fall on padding
+// are pointed past the buffer's end and receive zeros. Each lane's global offsets relative
+// to the tile's first row are computed once per kernel; per tile only the buffer resource's
+// base moves (scalar arithmetic). Rows past the end of the sequence arrive as zeros
+// through the buffer range check.
 #pragma once
 #include "attn_device.h"
 
@@ -28,65 +26,73 @@ namespace attn {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int D>
-__device__ __forceinline__ int swz_row(int r) {
-  if constexpr (D == 64) return (r ^ (r >> 3)) & 7;
-  else return r & 15;
-}
-template <int D>
-__device__ __forceinline__ int swz_tr(int r) {
-  const int j = r & 3;
-  if constexpr (D == 64) return 2 * j;
-  else return ((2 * j) ^ (4 * j)) & 15;
-}
+template <int D> __host__ __device__ constexpr int k_pitch() { return 2 * D + 16; }
+template <int D> __host__ __device__ constexpr int v_pitch() { return 2 * D + 64; }
 
-// Byte offset of the 16-byte chunk holding dims [8c, 8c+8) of row r.
-template <int D, bool TR>
-__device__ __forceinline__ int chunk_off(int r, int c) {
-  return r * (2 * D) + ((c ^ (TR ? swz_tr<D>(r) : swz_row<D>(r))) << 4);
-}
+// DMA plan of a ROWS x D tile with a padded row pitch (constants only; the per-lane offsets
+// live in a plain uint32_t[NPW] register array, filled by dma_init and used by dma_issue).
+template <int D, int ROWS, int PITCH, int NWAVES>
+struct DmaPlan {
+  static constexpr int CPRP = PITCH / 16;          // 16-byte slots per padded row
+  static constexpr int CPR = 2 * D / 16;           // data chunks per row
+  static constexpr int NI = ROWS * CPRP / 64;      // wave instructions per tile
+  static constexpr int NPW = (NI + NWAVES - 1) / NWAVES;
+  static constexpr int BYTES = ROWS * PITCH;
+  static_assert(ROWS * CPRP % 64 == 0, "tile must be whole DMA instructions");
+};
 
-// DMA one ROWS x D tile (rows row0 .. row0+ROWS-1 of the buffer view) into `dst`.
-// Each of the NWAVES waves issues ROWS*2*D/1024/NWAVES instructions.
-template <int D, int ROWS, bool TR, int NWAVES>
-__device__ __forceinline__ void dma_tile(char* dst, __amdgpu_buffer_rsrc_t rs, int row0, uint32_t row_bytes,
-                                         int wave, int lane) {
-  constexpr int KIB = ROWS * 2 * D / 1024;
-  static_assert(KIB % NWAVES == 0, "tile must split evenly over the waves");
-  constexpr int PER = KIB / NWAVES;
-  constexpr int NCH = D / 8;  // 16-byte chunks per row
+template <class Plan, int NWAVES>
+__device__ __forceinline__ void dma_init(uint32_t* voff, uint32_t row_bytes, int wave, int lane) {
 #pragma unroll
-  for (int it = 0; it < PER; ++it) {
-    const int blk = wave * PER + it;
-    const int byte = blk * 1024 + 16 * lane;
-    const int r = byte / (2 * D);
-    const int cp = (byte % (2 * D)) >> 4;
-    const int c = (cp ^ (TR ? swz_tr<D>(r) : swz_row<D>(r))) & (NCH - 1);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + blk * 1024), 16,
-                                             (uint32_t)(row0 + r) * row_bytes + c * 16, 0, 0, 0);
+  for (int t = 0; t < Plan::NPW; ++t) {
+    const int blk = wave + NWAVES * t;
+    const int g = blk * 64 + lane;
+    const int r = g / Plan::CPRP, cp = g % Plan::CPRP;
+    voff[t] = (blk < Plan::NI && cp < Plan::CPR) ? (uint32_t)r * row_bytes + cp * 16 : 0x80000000u;
   }
 }
 
-// Row read: dims 16*ks + 8*hf .. +7 of row r.
-template <int D>
-__device__ __forceinline__ u32x4 lds_row(const char* base, int r, int ks, int hf) {
-  return *(const u32x4*)(base + chunk_off<D, false>(r, 2 * ks + hf));
+// DMA of the tile whose first row is `row0` of the (batch, head) view starting at
+// `head_base` (`nrec` bytes valid from there). The buffer resource is built here: a
+// resource passed into a function template fails substitution in the host compilation
+// pass, which silently drops the kernel's launch stub.
+template <class Plan, int NWAVES>
+__device__ __forceinline__ void dma_issue(const uint32_t* voff, char* dst, const char* head_base,
+                                          int row0, uint32_t row_bytes, uint32_t nrec, int wave) {
+  const uint32_t off = (uint32_t)row0 * row_bytes;
+  const auto rs = make_rsrc(head_base + off, nrec - off);
+#pragma unroll
+  for (int t = 0; t < Plan::NPW; ++t) {
+    const int blk = wave + NWAVES * t;
+    if (Plan::NI % NWAVES == 0 || blk < Plan::NI)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + blk * 1024), 16, voff[t], 0, 0, 0);
+  }
 }
 
-// Transposed read for O^T += X^T P^T style products: lane l gets dim d0 + (l % 32) of the
-// 8 rows  rbase + 4*hf + {0,1,2,3}  and  rbase + 8 + 4*hf + {0,1,2,3}  (hf = l / 32), i.e.
-// the rows a 32x32 accumulator hands to k-slots 0..7 of lane half hf for the 16-row chunk
-// starting at rbase.
+// Lane base of K-tile row reads: row l%32, 16-byte chunk l/32 (add kb*32*pitch + ks*32).
 template <int D>
-__device__ __forceinline__ u32x4 lds_tr(const char* base, int rbase, int d0, int lane) {
+__device__ __forceinline__ int k_lane_off(int lane) { return (lane & 31) * k_pitch<D>() + (lane >> 5) * 16; }
+// Row read at a lane base: rows kb*32 + l%32, dims 16*ks + 8*(l/32) .. +7.
+template <int D>
+__device__ __forceinline__ u32x4 lds_k(const char* lane_base, int kb, int ks) {
+  return *(const u32x4*)(lane_base + kb * 32 * k_pitch<D>() + ks * 32);
+}
+
+// Lane base of V-tile transposed reads (see the layout note above).
+template <int D>
+__device__ __forceinline__ int v_lane_off(int lane) {
   const int i16 = lane & 15, grp = lane >> 4, hf = grp >> 1;
-  const int dcol = d0 + 16 * (grp & 1) + 4 * (i16 & 3);
-  const int ra = rbase + 4 * hf + (i16 >> 2);
-  const int rb = ra + 8;
-  const char* pa = base + chunk_off<D, true>(ra, dcol >> 3) + ((dcol & 7) << 1);
-  const char* pb = base + chunk_off<D, true>(rb, dcol >> 3) + ((dcol & 7) << 1);
+  return (4 * hf + (i16 >> 2)) * v_pitch<D>() + (16 * (grp & 1) + 4 * (i16 & 3)) * 2;
+}
+// Transposed read for O^T += V^T P^T: lane l gets dim 32*i + l%32 of rows
+// 16*c + 4*hf + {0..3} and 16*c + 8 + 4*hf + {0..3} (hf = l/32): the keys a 32x32 score
+// accumulator hands to k-slots 0..7 of lane half hf for the 16-key chunk c.
+template <int D>
+__device__ __forceinline__ u32x4 lds_vt(const char* lane_base, int c, int i) {
+  const char* pa = lane_base + c * 16 * v_pitch<D>() + i * 64;
   const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)pa);
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)pb);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(pa + 8 * v_pitch<D>()));
   const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
   return u32x4{ua[0], ua[1], ub[0], ub[1]};
 }
