@@ -232,12 +232,14 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
     float e[16 * NKB];
     float psum = 0.f;
     __builtin_amdgcn_sched_barrier(0);
+    // step t multiplies key block t % NKB at k-step t / NKB: consecutive MFMAs accumulate
+    // into different registers.
 #pragma unroll
-    for (int t = 0; t < PF; ++t) kop[t] = lds_k<D>(kn, t / NKS, t % NKS);
+    for (int t = 0; t < PF; ++t) kop[t] = lds_k<D>(kn, t % NKB, t / NKB);
 #pragma unroll
     for (int t = 0; t < S1; ++t) {
-      if (t + PF < S1) kop[t + PF] = lds_k<D>(kn, (t + PF) / NKS, (t + PF) % NKS);
-      const int kb = t / NKS, kk = t % NKS;
+      if (t + PF < S1) kop[t + PF] = lds_k<D>(kn, (t + PF) % NKB, (t + PF) / NKB);
+      const int kb = t % NKB, kk = t / NKB;
       nxt[kb] = mfma32x16<BF16>(kop[t], qreg[kk], kk == 0 ? f32x16{} : nxt[kb]);
 #pragma unroll
       for (int u = 0; u < EPS; ++u) {
@@ -255,12 +257,13 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
     l_run += psum;
     u32x4 vop[S2];
     float mx = -INFINITY;
+    // step t adds key chunk t / NDB into output block t % NDB (different accumulators in turn)
 #pragma unroll
-    for (int t = 0; t < PF; ++t) vop[t] = lds_vt<D>(vc, t % (2 * NKB), t / (2 * NKB));
+    for (int t = 0; t < PF; ++t) vop[t] = lds_vt<D>(vc, t / NDB, t % NDB);
 #pragma unroll
     for (int t = 0; t < S2; ++t) {
-      if (t + PF < S2) vop[t + PF] = lds_vt<D>(vc, (t + PF) % (2 * NKB), (t + PF) / (2 * NKB));
-      const int i = t / (2 * NKB), cidx = t % (2 * NKB);
+      if (t + PF < S2) vop[t + PF] = lds_vt<D>(vc, (t + PF) / NDB, (t + PF) % NDB);
+      const int i = t % NDB, cidx = t / NDB;
       oacc[i] = mfma32x16<BF16>(vop[t], pk[cidx], oacc[i]);
       // the row max of tile j+1, MPS scores per step
       if constexpr (MPS == 1) {
@@ -276,7 +279,10 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
     }
     mx = xhalf_max(mx);
     mx_next = mx * c;
-    wait_dma();
+    // V(j+1) must be in LDS before the barrier; K(j+2), issued after it, may stay in flight
+    // (every wave issued at least NI/4 of its instructions).
+    if (jj + 2 < nkt) wait_dma_keep<KPlan::NI / kWaves>();
+    else wait_dma();
     __syncthreads();
   };
   int j = 0;

@@ -98,5 +98,12 @@ __device__ __forceinline__ u32x4 lds_vt(const char* lane_base, int c, int i) {
 }
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's vector-memory operations are outstanding (the N most
+// recent ones may stay in flight across the following barrier).
+template <int N>
+__device__ __forceinline__ void wait_dma_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 }  // namespace attn
