@@ -20,8 +20,10 @@
 //     scalars, and dQ^T += K^T dS^T.
 // Recomputing S and dP in both 2 and 3 costs 7 matrix products instead of 5; the reported
 // FLOP rate still counts 2.5 forward passes.
+#include <type_traits>
+
 #include "attn_launch.h"
-#include "attn_tiles.h"
+#include "attn_lds.h"
 
 namespace attn {
 
@@ -73,24 +75,31 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- dK, dV
-template <int D> struct DkvCfg { static constexpr int BQ = 64; };
-template <> struct DkvCfg<256> { static constexpr int BQ = 32; };
+// KV-outer: 4 waves x 32 keys per workgroup. Each wave keeps its keys' K and V as MFMA B
+// operands in registers and its dK^T, dV^T accumulators in registers. Q and dO tiles of BQ
+// queries arrive by DMA in a two-stage LDS ring (pitch 2d+48: read as rows for S = Q K^T
+// and dP = dO V^T, read transposed for dV^T += dO^T P and dK^T += Q^T dS), with the
+// tile's L (log2 domain) and D staged beside them. S and dP put one key per lane, so P and
+// dS feed the next products straight from the accumulators. The 64-query tile is worked
+// in two 32-query halves so that the VALU work of one half runs under the other's MFMAs:
+// scores(0) | scores(1) + softmax(0) | update(0) + softmax(1) | update(1).
+template <int D> struct DkvCfg { static constexpr int BQ = 64, OCC = 1; };
+template <> struct DkvCfg<64> { static constexpr int BQ = 64, OCC = 2; };
+template <> struct DkvCfg<256> { static constexpr int BQ = 32, OCC = 1; };
 
 template <bool BF16, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int BQ = DkvCfg<D>::BQ;
   constexpr int NQB = BQ / 32;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
   constexpr int BKV = kWaves * 32;
-  using QT = Tile<D, BQ>;
-  constexpr int OFF_DO = QT::RM_BYTES;
-  constexpr int OFF_QT = 2 * QT::RM_BYTES;
-  constexpr int OFF_DOT = OFF_QT + QT::T_BYTES;
-  constexpr int OFF_L = OFF_DOT + QT::T_BYTES;
-  constexpr int OFF_D = OFF_L + BQ * 4;
-  constexpr int STAGE = OFF_D + BQ * 4;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  constexpr int QP = rt_pitch<D>();
+  using QPlan = DmaPlan<D, BQ, QP, kWaves>;
+  constexpr int TB = QPlan::BYTES;
+  constexpr int OFF_DO = TB, OFF_L = 2 * TB, OFF_D = 2 * TB + BQ * 4;
+  constexpr int STAGE = 2 * TB + 2 * BQ * 4;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -100,21 +109,47 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const int kt = work % nkvt;          // causal: low key tiles see the most queries; they go first
   const int bh = work / nkvt;
   const int h = bh % H, b = bh / H;
-  const int k0 = kt * BKV;
-  const int k0w = k0 + wave * 32;
+  const int k0w = kt * BKV + wave * 32;
   const int key = k0w + l32;
 
   const uint32_t row_bytes = (uint32_t)H * D * 2;
   const size_t head_off = ((size_t)b * N * H + h) * D * 2;
   const uint32_t nrec = (uint32_t)N * row_bytes - (uint32_t)h * D * 2;
-  const auto rq = make_rsrc((const char*)p.q + head_off, nrec);
   const auto rk = make_rsrc((const char*)p.k + head_off, nrec);
   const auto rv = make_rsrc((const char*)p.v + head_off, nrec);
-  const auto rdo = make_rsrc((const char*)p.dout + head_off, nrec);
   const auto rdk = make_rsrc((const char*)p.dk + head_off, nrec);
   const auto rdv = make_rsrc((const char*)p.dv + head_off, nrec);
+  const char* qbase = (const char*)p.q + head_off;
+  const char* dobase = (const char*)p.dout + head_off;
   const float* lse_h = p.lse + ((size_t)b * H + h) * N;
   const float* del_h = p.delta + ((size_t)b * H + h) * N;
+
+  const int nqt = (N + BQ - 1) / BQ;
+  const int qt0 = CAUSAL ? (kt * BKV) / BQ : 0;
+  uint32_t qvoff[QPlan::NPW];
+  dma_init<QPlan, kWaves>(qvoff, row_bytes, wave, lane);
+  float lval = 0.f, dval = 0.f;   // L (log2 domain) and D of query row (tile start + tid), tid < BQ
+  auto load_ld = [&](int qt) {
+    if (tid < BQ) {
+      const int q = qt * BQ + tid;
+      lval = q < N ? lse_h[q] * kLog2e : INFINITY;   // P = exp2(s*c - inf) = 0 past the end
+      dval = q < N ? del_h[q] : 0.f;
+    }
+  };
+  auto fetch = [&](int qt, int stage) {
+    char* st = smem + stage * STAGE;
+    dma_issue<QPlan, kWaves>(qvoff, st, qbase, qt * BQ, row_bytes, nrec, wave);
+    dma_issue<QPlan, kWaves>(qvoff, st + OFF_DO, dobase, qt * BQ, row_bytes, nrec, wave);
+    if (tid < BQ) {
+      ((float*)(st + OFF_L))[tid] = lval;
+      ((float*)(st + OFF_D))[tid] = dval;
+    }
+  };
+  if (qt0 < nqt) {
+    load_ld(qt0);
+    fetch(qt0, 0);
+    if (qt0 + 1 < nqt) load_ld(qt0 + 1);
+  }
 
   u32x4 kreg[NKS], vreg[NKS];
 #pragma unroll
@@ -122,32 +157,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     kreg[ks] = buf_load16(rk, (uint32_t)key * row_bytes + (16 * ks + 8 * hf) * 2);
     vreg[ks] = buf_load16(rv, (uint32_t)key * row_bytes + (16 * ks + 8 * hf) * 2);
   }
-
-  const int nqt = (N + BQ - 1) / BQ;
-  const int qt0 = CAUSAL ? k0 / BQ : 0;
-  QT tq, tdo;
-  float lval = 0.f, dval = 0.f;
-  auto load_tile = [&](int qt) {
-    tq.load(rq, qt * BQ, row_bytes, tid);
-    tdo.load(rdo, qt * BQ, row_bytes, tid);
-    if (tid < BQ) {
-      const int q = qt * BQ + tid;
-      lval = q < N ? lse_h[q] * kLog2e : INFINITY;   // P = exp2(s*c - inf) = 0 past the end
-      dval = q < N ? del_h[q] : 0.f;
-    }
-  };
-  auto store_tile = [&](int stage) {
-    char* st = smem + stage * STAGE;
-    tq.store_rowmajor(st, tid);
-    tdo.store_rowmajor(st + OFF_DO, tid);
-    tq.store_transposed(st + OFF_QT, tid);
-    tdo.store_transposed(st + OFF_DOT, tid);
-    if (tid < BQ) {
-      ((float*)(st + OFF_L))[tid] = lval;
-      ((float*)(st + OFF_D))[tid] = dval;
-    }
-  };
-
   f32x16 dkacc[NDB], dvacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) {
@@ -156,61 +165,114 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   }
   const bool wave_live = k0w < N;
   const float c = p.c;
+  const int row_q = row_lane_off<QP>(lane), tr_q = tr_lane_off<QP>(lane);
 
-  if (qt0 < nqt) {
-    load_tile(qt0);
-    store_tile(0);
-  }
+  wait_dma();
   __syncthreads();
+
+  auto tile = [&](const char* st, int q0, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    const char* qr = st + row_q;
+    const char* qtr = st + tr_q;
+    const char* dr = st + OFF_DO + row_q;
+    const char* dtr = st + OFF_DO + tr_q;
+    const float* ls = (const float*)(st + OFF_L);
+    const float* dls = (const float*)(st + OFF_D);
+    f32x16 s[NQB], dp[NQB];
+    u32x4 ppk[2 * NQB], dspk[2 * NQB];
+    // softmax(qb) element r: P and dS of query 8*(r/4) + 4*hf + r%4 of block qb
+    f32x4 l4{}, d4{};
+    auto sm_elem = [&](int qb, int r) {
+      if ((r & 3) == 0) {
+        l4 = *(const f32x4*)(ls + qb * 32 + 8 * (r >> 2) + 4 * hf);
+        d4 = *(const f32x4*)(dls + qb * 32 + 8 * (r >> 2) + 4 * hf);
+      }
+      float pv = fast_exp2(fmaf(s[qb][r], c, -l4[r & 3]));
+      if constexpr (EDGE) {
+        if (CAUSAL && key > q0 + qb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3)) pv = 0.f;
+      }
+      s[qb][r] = pv;
+      dp[qb][r] = pv * (dp[qb][r] - d4[r & 3]);
+      if ((r & 7) == 7) {
+        const int b8 = r - 7;
+        ppk[2 * qb + (r >> 3)] = u32x4{pack2<BF16>(s[qb][b8], s[qb][b8 + 1]), pack2<BF16>(s[qb][b8 + 2], s[qb][b8 + 3]),
+                                       pack2<BF16>(s[qb][b8 + 4], s[qb][b8 + 5]), pack2<BF16>(s[qb][b8 + 6], s[qb][b8 + 7])};
+        dspk[2 * qb + (r >> 3)] = u32x4{pack2<BF16>(dp[qb][b8], dp[qb][b8 + 1]), pack2<BF16>(dp[qb][b8 + 2], dp[qb][b8 + 3]),
+                                        pack2<BF16>(dp[qb][b8 + 4], dp[qb][b8 + 5]), pack2<BF16>(dp[qb][b8 + 6], dp[qb][b8 + 7])};
+      }
+    };
+    constexpr int SC = 2 * NKS;        // MFMAs of scores(qb): S and dP alternate
+    constexpr int UP = 2 * 2 * NDB;    // MFMAs of update(qb): dV and dK alternate over 2 chunks x NDB blocks
+    // The tile is one static sequence of MFMA steps: scores(0), scores(1), update(0), update(1)
+    // (NQB = 2) or scores(0), update(0) (NQB = 1). The LDS operand of step g is read PF
+    // steps ahead; the softmax of block 0 rides on scores(1), that of block 1 on update(0).
+    constexpr int T = NQB * (SC + UP);
+    constexpr int PF = 4;
+    auto operand = [&](int g) -> u32x4 {
+      if (g < NQB * SC) {
+        const int qb = g / SC, t = g % SC, kk = t >> 1;
+        return (t & 1) ? lds_row<QP>(dr, qb, kk) : lds_row<QP>(qr, qb, kk);
+      }
+      const int qb = (g - NQB * SC) / UP, t = (g - NQB * SC) % UP;
+      const int cc = 2 * qb + t / (2 * NDB), i = (t >> 1) % NDB;
+      return (t & 1) ? lds_tr<QP>(qtr, cc, i) : lds_tr<QP>(dtr, cc, i);
+    };
+    auto mfma_step = [&](int g, const u32x4& op) {
+      if (g < NQB * SC) {
+        const int qb = g / SC, t = g % SC, kk = t >> 1;
+        if (t & 1) dp[qb] = mfma32x16<BF16>(op, vreg[kk], kk == 0 ? f32x16{} : dp[qb]);
+        else s[qb] = mfma32x16<BF16>(op, kreg[kk], kk == 0 ? f32x16{} : s[qb]);
+      } else {
+        const int qb = (g - NQB * SC) / UP, t = (g - NQB * SC) % UP;
+        const int cc = 2 * qb + t / (2 * NDB), i = (t >> 1) % NDB;
+        if (t & 1) dkacc[i] = mfma32x16<BF16>(op, dspk[cc], dkacc[i]);
+        else dvacc[i] = mfma32x16<BF16>(op, ppk[cc], dvacc[i]);
+      }
+    };
+    u32x4 ring[PF + 1];
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<PF>([&](auto gc) { ring[decltype(gc)::value] = operand(decltype(gc)::value); });
+    static_for<T>([&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      if constexpr (NQB == 1 && g == SC) {
+        // single block: its softmax sits between the score and update steps
+        static_for<16>([&](auto rc) { sm_elem(0, decltype(rc)::value); });
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (g + PF < T) ring[(g + PF) % (PF + 1)] = operand(g + PF);
+      mfma_step(g, ring[g % (PF + 1)]);
+      if constexpr (NQB == 2) {
+        constexpr int ES = (16 + SC - 1) / SC, EU = (16 + UP - 1) / UP;   // softmax elements per step
+        if constexpr (g >= SC && g < 2 * SC) {
+          static_for<ES>([&](auto uc) {
+            constexpr int r = ES * (g - SC) + decltype(uc)::value;
+            if constexpr (r < 16) sm_elem(0, r);
+          });
+        } else if constexpr (g >= 2 * SC && g < 2 * SC + UP) {
+          static_for<EU>([&](auto uc) {
+            constexpr int r = EU * (g - 2 * SC) + decltype(uc)::value;
+            if constexpr (r < 16) sm_elem(1, r);
+          });
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
   for (int qt = qt0; qt < nqt; ++qt) {
-    const int stage = (qt - qt0) & 1;
-    const bool more = qt + 1 < nqt;
-    if (more) load_tile(qt + 1);
-    const char* st = smem + stage * STAGE;
+    const int i = qt - qt0;
+    if (qt + 1 < nqt) {
+      fetch(qt + 1, (i + 1) & 1);
+      if (qt + 2 < nqt) load_ld(qt + 2);
+    }
     const int q0 = qt * BQ;
     const bool skip = !wave_live || (CAUSAL && q0 + BQ - 1 < k0w);
     if (!skip) {
-      f32x16 s[NQB], dp[NQB];
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        s[qb] = f32x16{};
-        dp[qb] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < NKS; ++kk) {
-          s[qb] = mfma32x16<BF16>(read_rm<D>(st, qb * 32 + l32, kk, hf), kreg[kk], s[qb]);
-          dp[qb] = mfma32x16<BF16>(read_rm<D>(st + OFF_DO, qb * 32 + l32, kk, hf), vreg[kk], dp[qb]);
-        }
-      }
-      const bool edge = CAUSAL && q0 < k0w + 31;
-      const float* ls = (const float*)(st + OFF_L);
-      const float* ds_ = (const float*)(st + OFF_D);
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 l4 = *(const f32x4*)(ls + qb * 32 + 8 * g + 4 * hf);
-          const f32x4 d4 = *(const f32x4*)(ds_ + qb * 32 + 8 * g + 4 * hf);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            float pv = fast_exp2(fmaf(s[qb][r], c, -l4[e]));
-            if (edge && key > q0 + qb * 32 + 8 * g + 4 * hf + e) pv = 0.f;
-            s[qb][r] = pv;
-            dp[qb][r] = pv * (dp[qb][r] - d4[e]);
-          }
-        }
-#pragma unroll
-      for (int cc = 0; cc < BQ / 16; ++cc) {
-        const u32x4 ppk = pack_chunk<BF16>(s[cc >> 1], cc & 1);
-        const u32x4 dspk = pack_chunk<BF16>(dp[cc >> 1], cc & 1);
-#pragma unroll
-        for (int i = 0; i < NDB; ++i) {
-          dvacc[i] = mfma32x16<BF16>(read_t<BQ>(st + OFF_DOT, i * 32 + l32, cc, hf), ppk, dvacc[i]);
-          dkacc[i] = mfma32x16<BF16>(read_t<BQ>(st + OFF_QT, i * 32 + l32, cc, hf), dspk, dkacc[i]);
-        }
-      }
+      const char* st = smem + (i & 1) * STAGE;
+      if (CAUSAL && q0 < k0w + 31) tile(st, q0, std::true_type{});
+      else tile(st, q0, std::false_type{});
     }
-    if (more) store_tile(stage ^ 1);
+    wait_dma();
     __syncthreads();
   }
 
@@ -232,22 +294,27 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- dQ
-template <int D> struct DqCfg { static constexpr int BC = 64; };
-template <> struct DqCfg<64> { static constexpr int BC = 128; };
-template <> struct DqCfg<256> { static constexpr int BC = 32; };
+// Q-outer, like the forward: 4 waves x 32 query rows; K and V tiles arrive by DMA in a
+// two-stage LDS ring (padded rows). Per tile, three phases with their instructions
+// interleaved: S^T = K Q^T (K rows); dP^T = V dO^T (V rows) with P = exp2(s*c - L) on the
+// VALU underneath; dQ^T += K^T dS^T (K read transposed) with dS = P o (dP - D) of the next
+// 16-key chunk computed underneath. Tiles that touch the diagonal or the ragged end zero
+// the masked P explicitly.
+template <int D> struct DqCfg { static constexpr int BC = 64, OCC = 2; };
+template <> struct DqCfg<256> { static constexpr int BC = 32, OCC = 1; };
 
 template <bool BF16, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(BwdParams p) {
   constexpr int BC = DqCfg<D>::BC;
   constexpr int NKB = BC / 32;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
   constexpr int BR = kWaves * 32;
-  using KT = Tile<D, BC>;
-  constexpr int OFF_KT = KT::RM_BYTES;
-  constexpr int OFF_V = OFF_KT + KT::T_BYTES;
-  constexpr int STAGE = OFF_V + KT::RM_BYTES;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  constexpr int KP = rt_pitch<D>(), VP = k_pitch<D>();
+  using KPlan = DmaPlan<D, BC, KP, kWaves>;
+  using VPlan = DmaPlan<D, BC, VP, kWaves>;
+  constexpr int KB = KPlan::BYTES, VB = VPlan::BYTES, STAGE = KB + VB;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -265,10 +332,23 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   const size_t head_off = ((size_t)b * N * H + h) * D * 2;
   const uint32_t nrec = (uint32_t)N * row_bytes - (uint32_t)h * D * 2;
   const auto rq = make_rsrc((const char*)p.q + head_off, nrec);
-  const auto rk = make_rsrc((const char*)p.k + head_off, nrec);
-  const auto rv = make_rsrc((const char*)p.v + head_off, nrec);
   const auto rdo = make_rsrc((const char*)p.dout + head_off, nrec);
   const auto rdq = make_rsrc((const char*)p.dq + head_off, nrec);
+  const char* kbase = (const char*)p.k + head_off;
+  const char* vbase = (const char*)p.v + head_off;
+
+  const int kend = CAUSAL ? min(N, (qt + 1) * BR) : N;
+  const int nkt = (kend + BC - 1) / BC;
+  const int nkt_w = q0 >= N ? 0 : CAUSAL ? min(nkt, (q0 + 31) / BC + 1) : nkt;
+  uint32_t kvoff[KPlan::NPW], vvoff[VPlan::NPW];
+  dma_init<KPlan, kWaves>(kvoff, row_bytes, wave, lane);
+  dma_init<VPlan, kWaves>(vvoff, row_bytes, wave, lane);
+  auto fetch = [&](int j) {
+    char* st = smem + (j & 1) * STAGE;
+    dma_issue<KPlan, kWaves>(kvoff, st, kbase, j * BC, row_bytes, nrec, wave);
+    dma_issue<VPlan, kWaves>(vvoff, st + KB, vbase, j * BC, row_bytes, nrec, wave);
+  };
+  fetch(0);
 
   u32x4 qreg[NKS], doreg[NKS];
 #pragma unroll
@@ -278,74 +358,96 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   }
   const bool row_ok = qrow < N;
   const float lse2 = row_ok ? p.lse[((size_t)b * H + h) * N + qrow] * kLog2e : 0.f;
-  const float dq_row = row_ok ? p.delta[((size_t)b * H + h) * N + qrow] : 0.f;
-
-  const int kend = CAUSAL ? min(N, (qt + 1) * BR) : N;
-  const int nkt = (kend + BC - 1) / BC;
-  KT tk, tv;
-  auto load_tile = [&](int k0) {
-    tk.load(rk, k0, row_bytes, tid);
-    tv.load(rv, k0, row_bytes, tid);
-  };
-  auto store_tile = [&](int stage) {
-    char* st = smem + stage * STAGE;
-    tk.store_rowmajor(st, tid);
-    tk.store_transposed(st + OFF_KT, tid);
-    tv.store_rowmajor(st + OFF_V, tid);
-  };
+  const float drow = row_ok ? p.delta[((size_t)b * H + h) * N + qrow] : 0.f;
 
   f32x16 dqacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dqacc[i] = f32x16{};
-  const bool wave_live = q0 < N;
   const float c = p.c;
+  const int row_k = row_lane_off<KP>(lane), tr_k = tr_lane_off<KP>(lane), row_v = row_lane_off<VP>(lane);
 
-  load_tile(0);
-  store_tile(0);
+  wait_dma();
   __syncthreads();
-  for (int j = 0; j < nkt; ++j) {
-    const int k0 = j * BC;
-    const bool more = j + 1 < nkt;
-    if (more) load_tile(k0 + BC);
+
+  constexpr int S1 = NKB * NKS;            // MFMAs per score product
+  constexpr int EPS = 16 * NKB / S1;       // exponentials per dP step
+  constexpr int PF = 3;
+  auto tile = [&](int j, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
     const char* st = smem + (j & 1) * STAGE;
-    const bool skip = !wave_live || (CAUSAL && k0 > q0 + 31);
-    if (!skip) {
-      f32x16 s[NKB], dp[NKB];
+    const char* kr = st + row_k;
+    const char* kt = st + tr_k;
+    const char* vr = st + KB + row_v;
+    const int k0 = j * BC;
+    f32x16 s[NKB], dp[NKB];
+    u32x4 op[S1];
+    // phase 1: S^T = K Q^T
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        s[kb] = f32x16{};
-        dp[kb] = f32x16{};
+    for (int t = 0; t < PF; ++t) op[t] = lds_row<KP>(kr, t % NKB, t / NKB);
 #pragma unroll
-        for (int kk = 0; kk < NKS; ++kk) {
-          s[kb] = mfma32x16<BF16>(read_rm<D>(st, kb * 32 + l32, kk, hf), qreg[kk], s[kb]);
-          dp[kb] = mfma32x16<BF16>(read_rm<D>(st + OFF_V, kb * 32 + l32, kk, hf), doreg[kk], dp[kb]);
-        }
-      }
-      const bool edge = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pv = fast_exp2(fmaf(s[kb][r], c, -lse2));
-          if (edge) {
-            const int kidx = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (kidx >= N || (CAUSAL && kidx > qrow)) pv = 0.f;
-          }
-          s[kb][r] = pv * (dp[kb][r] - dq_row);
-        }
-#pragma unroll
-      for (int cc = 0; cc < BC / 16; ++cc) {
-        const u32x4 dspk = pack_chunk<BF16>(s[cc >> 1], cc & 1);
-#pragma unroll
-        for (int i = 0; i < NDB; ++i)
-          dqacc[i] = mfma32x16<BF16>(read_t<BC>(st + OFF_KT, i * 32 + l32, cc, hf), dspk, dqacc[i]);
-      }
+    for (int t = 0; t < S1; ++t) {
+      if (t + PF < S1) op[t + PF] = lds_row<KP>(kr, (t + PF) % NKB, (t + PF) / NKB);
+      const int kb = t % NKB, kk = t / NKB;
+      s[kb] = mfma32x16<BF16>(op[t], qreg[kk], kk == 0 ? f32x16{} : s[kb]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) store_tile((j + 1) & 1);
+    // phase 2: dP^T = V dO^T, with P on the VALU
+#pragma unroll
+    for (int t = 0; t < PF; ++t) op[t] = lds_row<VP>(vr, t % NKB, t / NKB);
+#pragma unroll
+    for (int t = 0; t < S1; ++t) {
+      if (t + PF < S1) op[t + PF] = lds_row<VP>(vr, (t + PF) % NKB, (t + PF) / NKB);
+      const int kb = t % NKB, kk = t / NKB;
+      dp[kb] = mfma32x16<BF16>(op[t], doreg[kk], kk == 0 ? f32x16{} : dp[kb]);
+#pragma unroll
+      for (int u = 0; u < EPS; ++u) {
+        const int i = EPS * t + u;
+        float pv = fast_exp2(fmaf(s[i >> 4][i & 15], c, -lse2));
+        if constexpr (EDGE) {
+          const int key = k0 + (i >> 4) * 32 + 8 * ((i & 15) >> 2) + 4 * hf + (i & 3);
+          if (key >= N || (CAUSAL && key > qrow)) pv = 0.f;
+        }
+        s[i >> 4][i & 15] = pv;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // phase 3: dQ^T += K^T dS^T, dS of chunk c+1 computed under chunk c's MFMAs
+    u32x4 dspk[BC / 16];
+    auto ds_chunk = [&](int cc) {
+      const int kb = cc >> 1, base = (cc & 1) * 8;
+      float v[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) v[t] = s[kb][base + t] * (dp[kb][base + t] - drow);
+      dspk[cc] = u32x4{pack2<BF16>(v[0], v[1]), pack2<BF16>(v[2], v[3]), pack2<BF16>(v[4], v[5]), pack2<BF16>(v[6], v[7])};
+    };
+    u32x4 kop[BC / 16 * NDB];
+#pragma unroll
+    for (int t = 0; t < PF; ++t) kop[t] = lds_tr<KP>(kt, t / NDB, t % NDB);
+    ds_chunk(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < BC / 16 * NDB; ++t) {
+      if (t + PF < BC / 16 * NDB) kop[t + PF] = lds_tr<KP>(kt, (t + PF) / NDB, (t + PF) % NDB);
+      const int cc = t / NDB, i = t % NDB;
+      dqacc[i] = mfma32x16<BF16>(kop[t], dspk[cc], dqacc[i]);
+      if (i == NDB - 1 && cc + 1 < BC / 16) ds_chunk(cc + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  for (int j = 0; j < nkt; ++j) {
+    if (j + 1 < nkt) fetch(j + 1);
+    if (j < nkt_w) {
+      const int k0 = j * BC;
+      if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0)) tile(j, std::true_type{});
+      else tile(j, std::false_type{});
+    }
+    wait_dma();
     __syncthreads();
   }
 
-  if (wave_live) {
+  if (nkt_w > 0) {
     const float scale = p.scale;
 #pragma unroll
     for (int i = 0; i < NDB; ++i)
@@ -356,6 +458,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
                           pack2<BF16>(dqacc[i][4 * rr + 2] * scale, dqacc[i][4 * rr + 3] * scale)};
         buf_store8(rdq, (uint32_t)qrow * row_bytes + d0 * 2, vv);
       }
+  } else if (q0 < N) {
+    // a wave whose rows see no key tile (cannot happen for equal query/key lengths) writes zeros
   }
 }
 

@@ -13,6 +13,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace attn {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -87,6 +90,18 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
   const int q = nblk >> 3, r = nblk & 7;
   const int x = bid & 7, i = bid >> 3;
   return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>{}) for I = 0 .. N-1, fully expanded
+// (unlike #pragma unroll, which gives up on large bodies and leaves register arrays
+// dynamically indexed).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 }  // namespace attn

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
   using VPlan = DmaPlan<D, BC, v_pitch<D>(), kWaves>;
 
   // K ring (2 stages, fetched two tiles ahead) then V ring (2 stages, one tile ahead).
-  constexpr int KBYTES = BC * k_pitch<D>(), VBYTES = BC * v_pitch<D>();
+  constexpr int KBYTES = KPlan::BYTES, VBYTES = VPlan::BYTES;
   __shared__ __attribute__((aligned(1024))) char smem[2 * KBYTES + 2 * VBYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;

@@ -33,12 +33,13 @@ template <int D> __host__ __device__ constexpr int v_pitch() { return 2 * D + 64
 // live in a plain uint32_t[NPW] register array, filled by dma_init and used by dma_issue).
 template <int D, int ROWS, int PITCH, int NWAVES>
 struct DmaPlan {
-  static constexpr int CPRP = PITCH / 16;          // 16-byte slots per padded row
-  static constexpr int CPR = 2 * D / 16;           // data chunks per row
-  static constexpr int NI = ROWS * CPRP / 64;      // wave instructions per tile
+  static constexpr int CPRP = PITCH / 16;             // 16-byte slots per padded row
+  static constexpr int CPR = 2 * D / 16;              // data chunks per row
+  static constexpr int SLOTS = ROWS * CPRP;
+  static constexpr int NI = (SLOTS + 63) / 64;        // wave instructions per tile
   static constexpr int NPW = (NI + NWAVES - 1) / NWAVES;
-  static constexpr int BYTES = ROWS * PITCH;
-  static_assert(ROWS * CPRP % 64 == 0, "tile must be whole DMA instructions");
+  static constexpr int BYTES = NI * 1024;             // LDS taken (the last instruction may overhang the tile)
+  static_assert(PITCH % 16 == 0, "pitch must be whole 16-byte slots");
 };
 
 template <class Plan, int NWAVES>
@@ -48,7 +49,7 @@ __device__ __forceinline__ void dma_init(uint32_t* voff, uint32_t row_bytes, int
     const int blk = wave + NWAVES * t;
     const int g = blk * 64 + lane;
     const int r = g / Plan::CPRP, cp = g % Plan::CPRP;
-    voff[t] = (blk < Plan::NI && cp < Plan::CPR) ? (uint32_t)r * row_bytes + cp * 16 : 0x80000000u;
+    voff[t] = (blk < Plan::NI && g < Plan::SLOTS && cp < Plan::CPR) ? (uint32_t)r * row_bytes + cp * 16 : 0x80000000u;
   }
 }
 
@@ -69,33 +70,43 @@ __device__ __forceinline__ void dma_issue(const uint32_t* voff, char* dst, const
   }
 }
 
-// Lane base of K-tile row reads: row l%32, 16-byte chunk l/32 (add kb*32*pitch + ks*32).
-template <int D>
-__device__ __forceinline__ int k_lane_off(int lane) { return (lane & 31) * k_pitch<D>() + (lane >> 5) * 16; }
-// Row read at a lane base: rows kb*32 + l%32, dims 16*ks + 8*(l/32) .. +7.
-template <int D>
-__device__ __forceinline__ u32x4 lds_k(const char* lane_base, int kb, int ks) {
-  return *(const u32x4*)(lane_base + kb * 32 * k_pitch<D>() + ks * 32);
+// Generic forms for a tile of row pitch PITCH bytes.
+// Row reads (MFMA operand over dims): lane base l%32 rows, 16-byte chunk l/32; then
+// rows blk*32 + l%32, dims 16*ks + 8*(l/32) .. +7 are at base + blk*32*PITCH + ks*32.
+template <int PITCH>
+__device__ __forceinline__ int row_lane_off(int lane) { return (lane & 31) * PITCH + (lane >> 5) * 16; }
+template <int PITCH>
+__device__ __forceinline__ u32x4 lds_row(const char* lane_base, int blk, int ks) {
+  return *(const u32x4*)(lane_base + blk * 32 * PITCH + ks * 32);
 }
-
-// Lane base of V-tile transposed reads (see the layout note above).
-template <int D>
-__device__ __forceinline__ int v_lane_off(int lane) {
+// Transposed reads (MFMA operand over rows): lane l gets dim 32*i + l%32 of rows
+// 16*c + 4*hf + {0..3} and 16*c + 8 + 4*hf + {0..3} (hf = l/32), i.e. the rows a 32x32
+// accumulator hands to k-slots 0..7 of lane half hf for the 16-row chunk c.
+template <int PITCH>
+__device__ __forceinline__ int tr_lane_off(int lane) {
   const int i16 = lane & 15, grp = lane >> 4, hf = grp >> 1;
-  return (4 * hf + (i16 >> 2)) * v_pitch<D>() + (16 * (grp & 1) + 4 * (i16 & 3)) * 2;
+  return (4 * hf + (i16 >> 2)) * PITCH + (16 * (grp & 1) + 4 * (i16 & 3)) * 2;
 }
-// Transposed read for O^T += V^T P^T: lane l gets dim 32*i + l%32 of rows
-// 16*c + 4*hf + {0..3} and 16*c + 8 + 4*hf + {0..3} (hf = l/32): the keys a 32x32 score
-// accumulator hands to k-slots 0..7 of lane half hf for the 16-key chunk c.
-template <int D>
-__device__ __forceinline__ u32x4 lds_vt(const char* lane_base, int c, int i) {
-  const char* pa = lane_base + c * 16 * v_pitch<D>() + i * 64;
+template <int PITCH>
+__device__ __forceinline__ u32x4 lds_tr(const char* lane_base, int c, int i) {
+  const char* pa = lane_base + c * 16 * PITCH + i * 64;
   const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)pa);
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(pa + 8 * v_pitch<D>()));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(pa + 8 * PITCH));
   const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
   return u32x4{ua[0], ua[1], ub[0], ub[1]};
 }
+// Pitch for tiles read both ways: rows conflict-free, transposed reads 2-way.
+template <int D> __host__ __device__ constexpr int rt_pitch() { return 2 * D + 48; }
+
+// Forward-kernel aliases: K tiles are read as rows, V tiles transposed.
+template <int D>
+__device__ __forceinline__ int k_lane_off(int lane) { return row_lane_off<k_pitch<D>()>(lane); }
+template <int D>
+__device__ __forceinline__ u32x4 lds_k(const char* lane_base, int kb, int ks) { return lds_row<k_pitch<D>()>(lane_base, kb, ks); }
+template <int D>
+__device__ __forceinline__ int v_lane_off(int lane) { return tr_lane_off<v_pitch<D>()>(lane); }
+template <int D>
+__device__ __forceinline__ u32x4 lds_vt(const char* lane_base, int c, int i) { return lds_tr<v_pitch<D>()>(lane_base, c, i); }
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Wait until at most N of this wave's vector-memory operations are outstanding (the N most
