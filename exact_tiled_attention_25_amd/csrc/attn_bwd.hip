@@ -101,7 +101,8 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
   constexpr int STAGE = 2 * TB + 2 * BQ * 4;
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps loop control scalar
   const int l32 = lane & 31, hf = lane >> 5;
   const int H = p.H, N = p.N;
   const int nkvt = (N + BKV - 1) / BKV;
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
     const int q0 = qt * BQ;
     const bool skip = !wave_live || (CAUSAL && q0 + BQ - 1 < k0w);
     if (!skip) {
-      const char* st = smem + (i & 1) * STAGE;
+      const char* st = smem + __builtin_amdgcn_readfirstlane((i & 1) * STAGE);
       if (CAUSAL && q0 < k0w + 31) tile(st, q0, std::true_type{});
       else tile(st, q0, std::false_type{});
     }
@@ -316,7 +317,8 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(BwdParams p)
   constexpr int KB = KPlan::BYTES, VB = VPlan::BYTES, STAGE = KB + VB;
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int H = p.H, N = p.N;
   const int nqt = (N + BR - 1) / BR;

@@ -95,6 +95,11 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
 // Compile-time loop: f(std::integral_constant<int, I>{}) for I = 0 .. N-1, fully expanded
 // (unlike #pragma unroll, which gives up on large bodies and leaves register arrays
 // dynamically indexed).
+// Ties a value to this point of the instruction stream: the arithmetic that produced it
+// cannot be sunk past later scheduling fences (used to keep VALU work under the MFMAs it
+// was placed beside).
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
 template <class F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
   (f(std::integral_constant<int, I>{}), ...);

@@ -7,12 +7,15 @@
 // L_i = m_i + log(l_i) ("Putting It Together", steps 2-7).
 //
 // gfx950 design (the Hopper producer/consumer, TMA and WGMMA machinery is prior art only):
-//  * 4 waves x 32 query rows = 128 rows per workgroup, two workgroups per CU (two waves per
-//    SIMD, so one wave's softmax runs while the other's MFMAs do); key tiles of BC = 64
-//    (d = 64: 128). d = 256 needs more than 256 registers and runs one wave per SIMD.
-//  * K and V tiles go from HBM straight into a two-stage LDS ring by DMA
-//    (buffer_load_dwordx4 ... lds), one tile ahead, with no register staging; one barrier
-//    per tile separates the stages. Rows past N arrive as zeros (buffer range check).
+//  * d = 64, 128: 8 waves x 32 query rows = 256 rows per workgroup, one workgroup per CU
+//    (two waves per SIMD, so one wave's softmax runs while the other's MFMAs do), sharing
+//    one three-stage K/V ring; key tiles of BC = 64. d = 256 needs more than 256 registers:
+//    4 waves (one per SIMD) and a two-stage ring.
+//  * K and V tiles go from HBM straight into the LDS ring by DMA (buffer_load_dwordx4 ...
+//    lds) with no register staging; with NS stages each tile is requested NS-2 loop
+//    iterations before the one whose end must see it landed, so the DMA latency hides under
+//    several tiles of work. One barrier per tile separates the stages. Rows past N arrive
+//    as zeros (buffer range check).
 //  * Scores are produced transposed, S^T = K Q^T (MFMA 32x32x16): each lane then owns ONE
 //    query row (column l%32 of the accumulator) and 16 keys of each 32-key block, so the
 //    row maximum is an in-lane reduction plus one permlane32 swap, and the row sum stays a
@@ -39,14 +42,14 @@ namespace attn {
 namespace {
 
 template <int D> struct FwdCfg;
-// BC: keys per tile; OCC: waves per SIMD the register budget is sized for.
-template <> struct FwdCfg<64> { static constexpr int BC = 64, OCC = 2; };
-template <> struct FwdCfg<128> { static constexpr int BC = 64, OCC = 2; };
-template <> struct FwdCfg<256> { static constexpr int BC = 64, OCC = 1; };
+// BC: keys per tile; WAVES: waves per workgroup (one workgroup per CU); STAGES: depth of
+// the K and V rings.
+template <> struct FwdCfg<64> { static constexpr int BC = 64, WAVES = 8, STAGES = 3; };
+template <> struct FwdCfg<128> { static constexpr int BC = 64, WAVES = 8, STAGES = 3; };
+template <> struct FwdCfg<256> { static constexpr int BC = 64, WAVES = 4, STAGES = 2; };
 
-constexpr int kWaves = 4;
 constexpr int kQW = 32;                  // query rows per wave
-constexpr int kBR = kWaves * kQW;        // query rows per workgroup
+template <int D> constexpr int fwd_rows() { return FwdCfg<D>::WAVES * kQW; }   // per workgroup
 constexpr float kTau = 8.0f;             // lazy-rescale threshold (log2 units)
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -118,19 +121,28 @@ __device__ __forceinline__ void tile_pv(f32x16 (&oacc)[D / 32], const char* vl, 
 }
 
 template <bool BF16, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(64 * FwdCfg<D>::WAVES, 1) void fwd_kernel(FwdParams p) {
   constexpr int BC = FwdCfg<D>::BC;
   constexpr int NKB = BC / 32;
   constexpr int NDB = D / 32;
   constexpr int NKS = D / 16;
+  constexpr int kWaves = FwdCfg<D>::WAVES;
+  constexpr int NS = FwdCfg<D>::STAGES;
+  constexpr int kBR = fwd_rows<D>();
   using KPlan = DmaPlan<D, BC, k_pitch<D>(), kWaves>;
   using VPlan = DmaPlan<D, BC, v_pitch<D>(), kWaves>;
+  // DMA instructions every wave issues per K / V tile (some issue one more)
+  constexpr int KMIN = KPlan::NI / kWaves, VMIN = VPlan::NI / kWaves;
+  static_assert(KMIN >= 1 && VMIN >= 1, "every wave takes part in each tile's DMA");
 
-  // K ring (2 stages, fetched two tiles ahead) then V ring (2 stages, one tile ahead).
+  // K ring then V ring, NS stages each. Tile t lives in stage t % NS. Loop iteration j
+  // reads K(j+1) and V(j), and requests V(j+NS-1) and K(j+NS) into the stages that
+  // iteration j-1 finished reading.
   constexpr int KBYTES = KPlan::BYTES, VBYTES = VPlan::BYTES;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * KBYTES + 2 * VBYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[NS * KBYTES + NS * VBYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps loop control scalar
   const int l32 = lane & 31, hf = lane >> 5;
   const int H = p.H, N = p.N;
   const int nqt = (N + kBR - 1) / kBR;
@@ -154,8 +166,10 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
   const int nkt = (kend + BC - 1) / BC;
   // tiles this wave computes: causal rows stop at the diagonal tile; rows past N compute none
   const int nkt_w = q0 >= N ? 0 : CAUSAL ? min(nkt, (q0 + kQW - 1) / BC + 1) : nkt;
-  auto kst = [&](int j) { return smem + (j & 1) * KBYTES; };
-  auto vst = [&](int j) { return smem + 2 * KBYTES + (j & 1) * VBYTES; };
+  // Stage offsets pass through readfirstlane: opaque to loop strength reduction, which would
+  // otherwise keep one induction register per operand address.
+  auto kst = [&](int j) { return smem + __builtin_amdgcn_readfirstlane((j % NS) * KBYTES); };
+  auto vst = [&](int j) { return smem + NS * KBYTES + __builtin_amdgcn_readfirstlane((j % NS) * VBYTES); };
   const int k_lane = k_lane_off<D>(lane), v_lane = v_lane_off<D>(lane);
   auto is_edge = [&](int j) { const int k0 = j * BC; return (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0); };
   uint32_t kvoff[KPlan::NPW], vvoff[VPlan::NPW];
@@ -163,14 +177,29 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
   dma_init<VPlan, kWaves>(vvoff, row_bytes, wave, lane);
   const char* kbase = (const char*)p.k + head_off;
   const char* vbase = (const char*)p.v + head_off;
-  dma_issue<KPlan, kWaves>(kvoff, kst(0), kbase, 0, row_bytes, nrec, wave);
-  dma_issue<VPlan, kWaves>(vvoff, vst(0), vbase, 0, row_bytes, nrec, wave);
-  if (nkt > 1) dma_issue<KPlan, kWaves>(kvoff, kst(1), kbase, BC, row_bytes, nrec, wave);
+  auto dma_k = [&](int t) { dma_issue<KPlan, kWaves>(kvoff, kst(t), kbase, t * BC, row_bytes, nrec, wave); };
+  auto dma_v = [&](int t) { dma_issue<VPlan, kWaves>(vvoff, vst(t), vbase, t * BC, row_bytes, nrec, wave); };
 
   // Q^T operand: lane holds query q0 + l32, dims 16*ks + 8*hf .. +7.
   u32x4 qreg[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) qreg[ks] = buf_load16(rq, (uint32_t)qrow * row_bytes + (16 * ks + 8 * hf) * 2);
+
+  // Prologue requests K(0), then the pairs V(t), K(t+1) for t = 0 .. NS-2; loop iteration
+  // j requests the pair V(j+NS-1), K(j+NS). Before iteration j (and before the loop, j = 0)
+  // K(j+1) and V(j) must have landed: everything but the pairs requested for t >= j+1 may
+  // stay in flight. This wave's share of a tile's DMA instructions: blocks wave, wave + W,
+  // ... below NI.
+  const int nk_w = KMIN + (wave < KPlan::NI % kWaves ? 1 : 0);
+  const int nv_w = VMIN + (wave < VPlan::NI % kWaves ? 1 : 0);
+  constexpr int KEEP_MAX = (NS - 2) * (KMIN + VMIN + 2);
+  auto wait_before = [&](int j) {   // wait until K(j+1) and V(j) are in LDS (this wave's part)
+    int keep = 0;
+#pragma unroll
+    for (int t = 1; t <= NS - 2; ++t) keep += (j + t < nkt ? nv_w : 0) + (j + t + 1 < nkt ? nk_w : 0);
+    wait_dma_keep_rt<KEEP_MAX>(keep);
+  };
+  dma_k(0);
 
   f32x16 oacc[NDB];
 #pragma unroll
@@ -178,7 +207,12 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c = p.c;
 
-  wait_dma();
+#pragma unroll
+  for (int t = 0; t <= NS - 2; ++t) {
+    if (t < nkt) dma_v(t);
+    if (t + 1 < nkt) dma_k(t + 1);
+  }
+  wait_before(0);
   __syncthreads();
 
   // Two-stage software pipeline (per wave): while the scores of tile j+1 are being
@@ -191,10 +225,17 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
     if (is_edge(0)) tile_mask<CAUSAL, NKB>(sc, 0, N, qrow, hf);
     mx_next = tile_max<NKB>(sc, c);
   }
+  // the first prefetch overwrites the stage of K(0), which the prologue just read
+  __syncthreads();
 
   auto prefetch = [&](int j) {
-    if (j + 1 < nkt) dma_issue<VPlan, kWaves>(vvoff, vst(j + 1), vbase, (j + 1) * BC, row_bytes, nrec, wave);
-    if (j + 2 < nkt) dma_issue<KPlan, kWaves>(kvoff, kst(j + 2), kbase, (j + 2) * BC, row_bytes, nrec, wave);
+    if (j + NS - 1 < nkt) dma_v(j + NS - 1);
+    if (j + NS < nkt) dma_k(j + NS);
+  };
+  // End of iteration j: iteration j+1 reads K(j+2) and V(j+1).
+  auto end_tile = [&](int j) {
+    wait_before(j + 1);
+    __syncthreads();
   };
   // the maximum of tile j (taken one step earlier) may move the reference: rescale O and l
   auto rescale = [&]() {
@@ -212,15 +253,20 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
 
   // Interior tiles (neither tile j nor j+1 masked; masking only ever starts near the end of
   // a wave's key range): the pipelined form, with the instruction order written out.
-  // Block 1 issues one S(j+1) MFMA per step and, under it, exponentiates two scores of
-  // tile j; block 2 issues one P~(j)V(j) MFMA per step with one max3 of tile j+1 under it.
+  // Block 1 issues one S(j+1) MFMA per step and, under it, exponentiates EPS scores of
+  // tile j (packing the first 16-key chunk of P~ as soon as it is complete). Block 2 issues
+  // one P~(j)V(j) MFMA per step and, under it, packs the next chunk of P~ (one conversion
+  // per step, ahead of the step that consumes it), adds the row-sum terms and folds tile
+  // j+1 into the row maximum. This splits the VALU work about evenly between the blocks.
   // LDS operands are fetched PF steps ahead; sched_barrier fences keep each step's order.
   constexpr int S1 = NKB * NKS;       // MFMAs in block 1
   constexpr int S2 = NDB * 2 * NKB;   // MFMAs in block 2
   constexpr int EPS = 16 * NKB / S1;  // scores exponentiated per block-1 step (256/d)
-  constexpr int MPS = 16 * NKB / S2;  // scores folded into the max per block-2 step (512/d)
-  constexpr int PF = 3;
-  static_assert(EPS * S1 == 16 * NKB && MPS * S2 == 16 * NKB && EPS >= 1 && MPS >= 1, "step split");
+  constexpr int MPS = 16 * NKB / S2;  // scores summed and folded into the max per block-2 step (512/d)
+  constexpr int PF = 2;
+  constexpr int C0 = 8 / EPS;         // block-1 step that packs the first conversion of chunk 0
+  static_assert(EPS * S1 == 16 * NKB && MPS * S2 == 16 * NKB && EPS >= 1 && (MPS == 1 || MPS % 2 == 0), "step split");
+  static_assert(C0 + 4 <= S1 && NDB % 2 == 0 && NDB <= 8, "chunk 0 packs inside block 1");
   auto fast_iter = [&](int jj, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) {
     prefetch(jj);
     rescale();
@@ -230,7 +276,8 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
     u32x4 pk[2 * NKB];
     u32x4 kop[S1];
     float e[16 * NKB];
-    float psum = 0.f;
+    // conversion u (0..3) of chunk q: two P~ values of keys 8q + 2u, 8q + 2u + 1
+    auto pack = [&](int q, int u) { pk[q][u] = pack2<BF16>(e[8 * q + 2 * u], e[8 * q + 2 * u + 1]); };
     __builtin_amdgcn_sched_barrier(0);
     // step t multiplies key block t % NKB at k-step t / NKB: consecutive MFMAs accumulate
     // into different registers.
@@ -245,18 +292,12 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
       for (int u = 0; u < EPS; ++u) {
         const int i = EPS * t + u;
         e[i] = fast_exp2(fmaf(cur[i >> 4][i & 15], c, -m_use));
-        psum += e[i];
       }
-      if ((EPS * (t + 1)) % 8 == 0) {
-        const int q = EPS * (t + 1) / 8 - 1;   // 8 scores -> one 16-key operand
-        pk[q] = u32x4{pack2<BF16>(e[8 * q + 0], e[8 * q + 1]), pack2<BF16>(e[8 * q + 2], e[8 * q + 3]),
-                      pack2<BF16>(e[8 * q + 4], e[8 * q + 5]), pack2<BF16>(e[8 * q + 6], e[8 * q + 7])};
-      }
+      if (t >= C0 && t < C0 + 4) pack(0, t - C0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    l_run += psum;
     u32x4 vop[S2];
-    float mx = -INFINITY;
+    float mx = -INFINITY, psum = 0.f;
     // step t adds key chunk t / NDB into output block t % NDB (different accumulators in turn)
 #pragma unroll
     for (int t = 0; t < PF; ++t) vop[t] = lds_vt<D>(vc, t / NDB, t % NDB);
@@ -265,25 +306,32 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
       if (t + PF < S2) vop[t + PF] = lds_vt<D>(vc, (t + PF) / NDB, (t + PF) % NDB);
       const int i = t % NDB, cidx = t / NDB;
       oacc[i] = mfma32x16<BF16>(vop[t], pk[cidx], oacc[i]);
-      // the row max of tile j+1, MPS scores per step
+      // chunk cidx + 1 is consumed from step NDB * (cidx + 1): convert it during chunk cidx,
+      // CPS conversions every SS-th step
+      constexpr int CPS = NDB >= 4 ? 1 : 4 / NDB, SS = NDB >= 4 ? NDB / 4 : 1;
+      if (cidx + 1 < 2 * NKB && (t % NDB) % SS == 0) {
+#pragma unroll
+        for (int v = 0; v < CPS; ++v) pack(cidx + 1, ((t % NDB) / SS) * CPS + v);
+      }
       if constexpr (MPS == 1) {
+        psum += e[t];
         mx = fmaxf(mx, nxt[t >> 4][t & 15]);
       } else {
 #pragma unroll
         for (int u = 0; u < MPS; u += 2) {
-          const int i = MPS * t + u;
-          mx = fmaxf(mx, fmaxf(nxt[i >> 4][i & 15], nxt[(i + 1) >> 4][(i + 1) & 15]));
+          const int i2 = MPS * t + u;
+          psum += e[i2];
+          psum += e[i2 + 1];
+          mx = fmaxf(mx, fmaxf(nxt[i2 >> 4][i2 & 15], nxt[(i2 + 1) >> 4][(i2 + 1) & 15]));
         }
       }
+      pin(psum);   // keep the sum's adds in this step (the compiler would sink them)
       __builtin_amdgcn_sched_barrier(0);
     }
+    l_run += psum;
     mx = xhalf_max(mx);
     mx_next = mx * c;
-    // V(j+1) must be in LDS before the barrier; K(j+2), issued after it, may stay in flight
-    // (every wave issued at least NI/4 of its instructions).
-    if (jj + 2 < nkt) wait_dma_keep<KPlan::NI / kWaves>();
-    else wait_dma();
-    __syncthreads();
+    end_tile(jj);
   };
   int j = 0;
   for (; j + 2 < nkt_w && !is_edge(j + 2); j += 2) {   // sc/sn swap roles: no copies
@@ -313,8 +361,7 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
         mx_next = tile_max<NKB>(sc, c);
       }
     }
-    wait_dma();
-    __syncthreads();
+    end_tile(j);
   }
 
   if (nkt_w > 0) {
@@ -336,9 +383,9 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_kernel(FwdParams p) {
 
 template <bool BF16, int D, bool CAUSAL>
 hipError_t launch_t(const FwdParams& p, hipStream_t s) {
-  const int nqt = (p.N + kBR - 1) / kBR;
+  const int nqt = (p.N + fwd_rows<D>() - 1) / fwd_rows<D>();
   const dim3 grid((unsigned)(p.B * p.H * nqt));
-  hipLaunchKernelGGL((fwd_kernel<BF16, D, CAUSAL>), grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((fwd_kernel<BF16, D, CAUSAL>), grid, dim3(64 * FwdCfg<D>::WAVES), 0, s, p);
   return hipGetLastError();
 }
 

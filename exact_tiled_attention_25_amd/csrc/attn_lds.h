@@ -117,4 +117,15 @@ __device__ __forceinline__ void wait_dma_keep() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// The same for a wave-uniform count 0 <= n <= MAX (s_waitcnt takes an immediate; counts
+// above MAX wait as for MAX, which only waits longer).
+template <int... I>
+__device__ __forceinline__ void wait_dma_keep_sel(int n, std::integer_sequence<int, I...>) {
+  ((n == I ? wait_dma_keep<I>() : void()), ...);
+}
+template <int MAX>
+__device__ __forceinline__ void wait_dma_keep_rt(int n) {
+  wait_dma_keep_sel(n < MAX ? n : MAX, std::make_integer_sequence<int, MAX + 1>{});
+}
+
 }  // namespace attn
