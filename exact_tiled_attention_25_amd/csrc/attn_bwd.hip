@@ -83,6 +83,27 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 // dS feed the next products straight from the accumulators. The 64-query tile is worked
 // in two 32-query halves so that the VALU work of one half runs under the other's MFMAs:
 // scores(0) | scores(1) + softmax(0) | update(0) + softmax(1) | update(1).
+// Step schedule of one Q tile in the dK/dV kernel (NQB 32-query blocks; SC score steps and
+// UP update steps per block): softmax elements per step (ES during the scores of block 1,
+// EU during the update of block 0) and the register ring that holds the L and D values of
+// query group (qb, m) from its LDS read, LPF steps ahead of its first use, to its last use.
+template <int NQB, int SC, int UP>
+struct DkvSched {
+  static constexpr int ES = (16 + SC - 1) / SC, EU = (16 + UP - 1) / UP;
+  static constexpr int LPF = 4;
+  static constexpr int LRS = NQB == 1 ? 4 : ES >= 2 ? 3 : 2;
+  static constexpr int use(int qb, int m, int last) {   // first (last = 0) or last step using the group
+    return NQB == 1 ? SC : qb == 0 ? SC + (4 * m + 3 * last) / ES : 2 * SC + (4 * m + 3 * last) / EU;
+  }
+  static constexpr int load(int qb, int m) { return use(qb, m, 0) - LPF; }
+  static constexpr bool ring_ok() {   // a slot is reloaded only after the last use of its group
+    for (int a = 0; a < 4 * NQB; ++a)
+      for (int b = a + 1; b < 4 * NQB; ++b)
+        if (a % LRS == b % LRS && load(b / 4, b % 4) <= use(a / 4, a % 4, 1)) return false;
+    return load(0, 0) >= 0;
+  }
+};
+
 template <int D> struct DkvCfg { static constexpr int BQ = 64, OCC = 1; };
 template <> struct DkvCfg<64> { static constexpr int BQ = 64, OCC = 2; };
 template <> struct DkvCfg<256> { static constexpr int BQ = 32, OCC = 1; };
@@ -158,6 +179,11 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
     kreg[ks] = buf_load16(rk, (uint32_t)key * row_bytes + (16 * ks + 8 * hf) * 2);
     vreg[ks] = buf_load16(rv, (uint32_t)key * row_bytes + (16 * ks + 8 * hf) * 2);
   }
+  // One wave per SIMD (512 registers): every MFMA accumulator (dK, dV for the whole kernel,
+  // S and dP per block) lives in AGPRs; K, V and everything the VALU writes in VGPRs.
+  // Without the hint the allocator shares AGPRs between S/dP and dK/dV and copies the
+  // evicted accumulators back and forth every tile.
+  constexpr bool PIN = DkvCfg<D>::OCC == 1;
   f32x16 dkacc[NDB], dvacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) {
@@ -181,13 +207,23 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
     const float* dls = (const float*)(st + OFF_D);
     f32x16 s[NQB], dp[NQB];
     u32x4 ppk[2 * NQB], dspk[2 * NQB];
+    // L and D of query group (qb, m) = queries 8m + 4hf .. +3 of block qb, read from LDS
+    // into a small register ring LPF steps before the softmax step that first needs them
+    // (reading them at the point of use would stall on the whole LDS queue every time).
+    constexpr int SC = 2 * NKS;        // MFMAs of scores(qb): S and dP alternate
+    constexpr int UP = 2 * 2 * NDB;    // MFMAs of update(qb): dV and dK alternate over 2 chunks x NDB blocks
+    using Sched = DkvSched<NQB, SC, UP>;
+    static_assert(Sched::ring_ok(), "L/D ring slot reused while live");
+    constexpr int ES = Sched::ES, EU = Sched::EU, LRS = Sched::LRS;
+    f32x4 lring[LRS], dring[LRS];
+    auto load_grp = [&](int qb, int m) {
+      lring[(4 * qb + m) % LRS] = *(const f32x4*)(ls + qb * 32 + 8 * m + 4 * hf);
+      dring[(4 * qb + m) % LRS] = *(const f32x4*)(dls + qb * 32 + 8 * m + 4 * hf);
+    };
     // softmax(qb) element r: P and dS of query 8*(r/4) + 4*hf + r%4 of block qb
-    f32x4 l4{}, d4{};
     auto sm_elem = [&](int qb, int r) {
-      if ((r & 3) == 0) {
-        l4 = *(const f32x4*)(ls + qb * 32 + 8 * (r >> 2) + 4 * hf);
-        d4 = *(const f32x4*)(dls + qb * 32 + 8 * (r >> 2) + 4 * hf);
-      }
+      const f32x4& l4 = lring[(4 * qb + (r >> 2)) % LRS];
+      const f32x4& d4 = dring[(4 * qb + (r >> 2)) % LRS];
       float pv = fast_exp2(fmaf(s[qb][r], c, -l4[r & 3]));
       if constexpr (EDGE) {
         if (CAUSAL && key > q0 + qb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3)) pv = 0.f;
@@ -202,8 +238,6 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
                                         pack2<BF16>(dp[qb][b8 + 4], dp[qb][b8 + 5]), pack2<BF16>(dp[qb][b8 + 6], dp[qb][b8 + 7])};
       }
     };
-    constexpr int SC = 2 * NKS;        // MFMAs of scores(qb): S and dP alternate
-    constexpr int UP = 2 * 2 * NDB;    // MFMAs of update(qb): dV and dK alternate over 2 chunks x NDB blocks
     // The tile is one static sequence of MFMA steps: scores(0), scores(1), update(0), update(1)
     // (NQB = 2) or scores(0), update(0) (NQB = 1). The LDS operand of step g is read PF
     // steps ahead; the softmax of block 0 rides on scores(1), that of block 1 on update(0).
@@ -221,13 +255,24 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
     auto mfma_step = [&](int g, const u32x4& op) {
       if (g < NQB * SC) {
         const int qb = g / SC, t = g % SC, kk = t >> 1;
-        if (t & 1) dp[qb] = mfma32x16<BF16>(op, vreg[kk], kk == 0 ? f32x16{} : dp[qb]);
-        else s[qb] = mfma32x16<BF16>(op, kreg[kk], kk == 0 ? f32x16{} : s[qb]);
+        if (t & 1) {
+          dp[qb] = mfma32x16<BF16>(op, vreg[kk], kk == 0 ? f32x16{} : dp[qb]);
+          if constexpr (PIN) pin_acc(dp[qb]);
+        } else {
+          s[qb] = mfma32x16<BF16>(op, kreg[kk], kk == 0 ? f32x16{} : s[qb]);
+          if constexpr (PIN) pin_acc(s[qb]);
+        }
+
       } else {
         const int qb = (g - NQB * SC) / UP, t = (g - NQB * SC) % UP;
         const int cc = 2 * qb + t / (2 * NDB), i = (t >> 1) % NDB;
-        if (t & 1) dkacc[i] = mfma32x16<BF16>(op, dspk[cc], dkacc[i]);
-        else dvacc[i] = mfma32x16<BF16>(op, ppk[cc], dvacc[i]);
+        if (t & 1) {
+          dkacc[i] = mfma32x16<BF16>(op, dspk[cc], dkacc[i]);
+          if constexpr (PIN) pin_acc(dkacc[i]);
+        } else {
+          dvacc[i] = mfma32x16<BF16>(op, ppk[cc], dvacc[i]);
+          if constexpr (PIN) pin_acc(dvacc[i]);
+        }
       }
     };
     u32x4 ring[PF + 1];
@@ -235,6 +280,10 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
     static_for<PF>([&](auto gc) { ring[decltype(gc)::value] = operand(decltype(gc)::value); });
     static_for<T>([&](auto gc) {
       constexpr int g = decltype(gc)::value;
+      static_for<NQB * 4>([&](auto mc) {
+        constexpr int qb = decltype(mc)::value / 4, m = decltype(mc)::value % 4;
+        if constexpr (Sched::load(qb, m) == g) load_grp(qb, m);
+      });
       if constexpr (NQB == 1 && g == SC) {
         // single block: its softmax sits between the score and update steps
         static_for<16>([&](auto rc) { sm_elem(0, decltype(rc)::value); });
@@ -243,7 +292,6 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
       if constexpr (g + PF < T) ring[(g + PF) % (PF + 1)] = operand(g + PF);
       mfma_step(g, ring[g % (PF + 1)]);
       if constexpr (NQB == 2) {
-        constexpr int ES = (16 + SC - 1) / SC, EU = (16 + UP - 1) / UP;   // softmax elements per step
         if constexpr (g >= SC && g < 2 * SC) {
           static_for<ES>([&](auto uc) {
             constexpr int r = ES * (g - SC) + decltype(uc)::value;
@@ -260,22 +308,43 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
     });
   };
 
-  for (int qt = qt0; qt < nqt; ++qt) {
+  auto pin_all = [&]() {
+    if constexpr (PIN) {
+#pragma unroll
+      for (int a = 0; a < NDB; ++a) {
+        pin_acc(dkacc[a]);
+        pin_acc(dvacc[a]);
+      }
+    }
+  };
+  // Causal: the first tiles (those that reach a key of this workgroup) need the mask, and
+  // waves whose keys all follow the tile skip it; the rest need neither. Two loops keep each
+  // loop body straight-line (one tile form, no skip branch), so the accumulators stay put.
+  // Waves past the end of the sequence compute on zero-filled K, V and store nothing.
+  auto step = [&](int qt, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    pin_all();
     const int i = qt - qt0;
     if (qt + 1 < nqt) {
       fetch(qt + 1, (i + 1) & 1);
       if (qt + 2 < nqt) load_ld(qt + 2);
     }
     const int q0 = qt * BQ;
-    const bool skip = !wave_live || (CAUSAL && q0 + BQ - 1 < k0w);
-    if (!skip) {
-      const char* st = smem + __builtin_amdgcn_readfirstlane((i & 1) * STAGE);
-      if (CAUSAL && q0 < k0w + 31) tile(st, q0, std::true_type{});
-      else tile(st, q0, std::false_type{});
+    const char* st = smem + __builtin_amdgcn_readfirstlane((i & 1) * STAGE);
+    if constexpr (EDGE) {
+      if (wave_live && q0 + BQ - 1 >= k0w) tile(st, q0, std::true_type{});
+    } else {
+      tile(st, q0, std::false_type{});
     }
     wait_dma();
     __syncthreads();
+    pin_all();
+  };
+  int qt = qt0;
+  if constexpr (CAUSAL) {
+    for (; qt < nqt && qt * BQ < kt * BKV + BKV - 1; ++qt) step(qt, std::true_type{});
   }
+  for (; qt < nqt; ++qt) step(qt, std::false_type{});
 
   if (wave_live) {
     const float scale = p.scale;

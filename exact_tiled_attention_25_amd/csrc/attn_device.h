@@ -99,6 +99,14 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
 // cannot be sunk past later scheduling fences (used to keep VALU work under the MFMAs it
 // was placed beside).
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+// Ties an MFMA accumulator to the accumulation register file (AGPRs). Accumulators that
+// live across a whole loop and are only touched by MFMAs belong there; without the hint
+// the allocator may park them in VGPRs and copy them over before every MFMA.
+__device__ __forceinline__ void pin_acc(f32x16& x) { asm volatile("" : "+a"(x)); }
+// ... and an MFMA operand held in registers for a whole loop (MFMAs read AGPR operands).
+__device__ __forceinline__ void pin_acc(u32x4& x) { asm volatile("" : "+a"(x)); }
+// An MFMA result that the VALU consumes next stays in VGPRs.
+__device__ __forceinline__ void pin_vgpr(f32x16& x) { asm volatile("" : "+v"(x)); }
 
 template <class F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
