@@ -28,6 +28,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 // Buffer resource word 3 for raw (untyped) gfx9 buffer accesses: DATA_FORMAT = 32 bit.
 // Loads past num_records return zero and stores past it are dropped.

@@ -15,19 +15,12 @@
 //   after clamping to +-448 (the hardware convert is not saturating).
 //
 // fwd_fp8_kernel: the bf16 forward's structure with v_mfma_f32_32x32x64_f8f6f4 (e4m3 x
-//   e4m3, fp32 accumulate), 128-key tiles = two 64-key products.
-//  * S^T = K8 Q8^T: lane owns a query; Q and K descales fold into one per-lane, per-64-key
-//    coefficient of the exp2 argument (scores scaled by scale*log2(e)*dq*dk).
-//  * One 64-key PV product consumes exactly two 32-key score accumulators (32 fp8 bytes per
-//    lane). Byte b of lane half h is key 32*(b/16) + 8*((b%16)/4) + 4*h + b%4, so V^T sits
-//    in LDS with position bits [5:2] = rotr4(key bits [5:2]).
-//  * The V descale of each 64-key block enters the exp2 argument as log2(64*dv/dv_max),
-//    dv_max being the head's largest V descale; the row sum l still counts the unweighted
-//    P~, and the epilogue multiplies O by dv_max/64/l. The lazy-rescale threshold is 2^2, so
-//    the fp8 operand P~*64*dv/dv_max stays in [0, 256], inside e4m3's normal range down to
-//    P~ = 2^-12.
-#include "attn_device.h"
+//   e4m3, fp32 accumulate) on 64-key tiles (one K and one V scale block each): DMA ring,
+//   S^T = K8 Q8^T with one query per lane, P~ packed to fp8 straight from the score
+//   accumulators, V^T gathered by 8-bit transpose reads in the accumulators' key order,
+//   the V descale folded into the exp2 argument (details at the kernel).
 #include "attn_launch.h"
+#include "attn_lds.h"
 
 namespace attn {
 
@@ -130,47 +123,90 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(Fp8QuantParams p) {
 }
 
 // ---------------------------------------------------------------- fp8 attention
-constexpr int kWaves = 4;
-constexpr int kQW = 32;
-constexpr int kBR = kWaves * kQW;
-constexpr int kBC = 128;              // keys per tile
+template <int D> struct Fp8Cfg;
+// WAVES: waves per workgroup (one workgroup per CU); STAGES: depth of the K and V rings.
+template <> struct Fp8Cfg<64> { static constexpr int WAVES = 8, STAGES = 3; };
+template <> struct Fp8Cfg<128> { static constexpr int WAVES = 8, STAGES = 3; };
+template <> struct Fp8Cfg<256> { static constexpr int WAVES = 4, STAGES = 3; };
+constexpr int kQW8 = 32;              // query rows per wave
+template <int D> constexpr int fp8_rows() { return Fp8Cfg<D>::WAVES * kQW8; }
+constexpr int kBC8 = 64;              // keys per tile: one K and one V scale block
 constexpr float kTau8 = 2.0f;         // lazy-rescale threshold (log2 units)
 constexpr float kPScale = 64.0f;      // P~ * 64 * dv/dv_max is the fp8 PV operand
-constexpr float kLog2PScale = 6.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
+// K and V tiles: row-major e4m3 rows of D bytes at pitch D + 16 (16-byte row offset mod
+// 256: the K row reads of a 16-lane group and the V transpose reads are conflict-free).
+template <int D> __host__ __device__ constexpr int f8_pitch() { return D + 16; }
 
 __device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// position (0..63) of key group 4*m .. 4*m+3 inside a 64-key chunk
-__device__ __forceinline__ int fp8_vpos(int key) {
-  const int k4 = (key >> 2) & 15;                       // key bits [5:2]
-  const int p4 = ((k4 >> 1) | ((k4 & 1) << 3)) & 15;   // rotate right by one
-  return (p4 << 2) | (key & 3);
+// K operand of S^T = K Q^T: lane l holds key row kb*32 + l%32, dims 64*ks + 32*(l/32) .. +31.
+template <int P>
+__device__ __forceinline__ int k8_lane_off(int lane) { return (lane & 31) * P + (lane >> 5) * 32; }
+template <int P>
+__device__ __forceinline__ i32x8 lds_k8(const char* lane_base, int kb, int ks) {
+  const char* a = lane_base + kb * 32 * P + ks * 64;
+  const u32x4 x = *(const u32x4*)a, y = *(const u32x4*)(a + 16);
+  return i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+}
+// V^T operand of O^T += V^T P^T, gathered from the row-major V tile by four 8-bit transpose
+// reads (ds_read_b64_tr_b8: within each 16-lane group, lane i receives byte i%8 of the 8-byte
+// pieces of source lanes 2e + i/8, e = 0..7, as its byte e). The P operand taken straight
+// from two 32-key score accumulators holds, in byte b of lane half h, key
+// 32*(b/16) + 8*((b%16)/4) + 4*h + b%4; so source lane s of read j points at key
+// 16j + 8*(s/8) + 4*h + (s/2)%4 and dims 16*((l/16)%2) + 8*(s%2), and lane l receives dim
+// l%32 (plus 32*i for output block i) of exactly the keys of its P bytes 8j .. 8j+7.
+template <int P>
+__device__ __forceinline__ int vt8_lane_off(int lane) {
+  const int s = lane & 15, h = lane >> 5;
+  return (8 * (s >> 3) + 4 * h + ((s >> 1) & 3)) * P + 16 * ((lane >> 4) & 1) + 8 * (s & 1);
+}
+template <int P>
+__device__ __forceinline__ i32x8 lds_vt8(const char* lane_base, int i) {
+  i32x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const i32x2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) i32x2*)(lane_base + 16 * j * P + 32 * i));
+    r[2 * j] = t[0];
+    r[2 * j + 1] = t[1];
+  }
+  return r;
 }
 
-__device__ __forceinline__ int fp8_vswz(int d) { return (d >> 1) & 7; }
-
+// One workgroup per (query tile, head, batch), the bf16 forward's structure in fp8:
+//  * S^T = K8 Q8^T (v_mfma_f32_32x32x64_f8f6f4, fp32 accumulate): lane owns a query; the Q
+//    and K descales fold into one per-lane, per-tile coefficient of the exp2 argument
+//    (scores scaled by scale*log2(e)*dq*dk).
+//  * One 64-key PV product consumes exactly the tile's two 32-key score accumulators (32 fp8
+//    bytes per lane) against the V^T operand read by transpose reads (see lds_vt8).
+//  * The V descale of the tile enters the exp2 argument as log2(64*dv/dv_max), dv_max being
+//    the head's largest V descale; the row sum l counts the unweighted P~, and the epilogue
+//    multiplies O by dv_max/64/l. The lazy-rescale threshold is 2^2, so the fp8 operand
+//    P~*64*dv/dv_max stays in [0, 256], inside e4m3's range.
+//  * K and V tiles arrive by DMA in a three-stage LDS ring; the pipelined loop forms
+//    S(j+1) on the matrix cores while the VALU exponentiates tile j, then P~(j) V(j) while
+//    the VALU sums tile j and takes the row maximum of tile j+1.
 template <bool OUT_BF16, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_fp8_kernel(Fp8FwdParams p) {
-  constexpr int BC = kBC;
-  constexpr int KP = D + 16;                 // K8 row pitch (bytes)
-  constexpr int KBYTES = BC * KP;
-  constexpr int VP = BC;                     // V^T row pitch (bytes)
-  constexpr int VBYTES = D * VP;
-  constexpr int STAGE = KBYTES + VBYTES;
-  constexpr int NKS = D / 64;
-  constexpr int NKB = BC / 32;
-  constexpr int NC2 = BC / 64;
-  constexpr int NDB = D / 32;
-  constexpr int KIT = BC * D / 16 / 256;
-  constexpr int VITEMS = (BC / 4) * (D / 16);
-  constexpr int VIT = (VITEMS + 255) / 256;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+__global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8FwdParams p) {
+  constexpr int kWaves = Fp8Cfg<D>::WAVES;
+  constexpr int NS = Fp8Cfg<D>::STAGES;
+  constexpr int kBR = fp8_rows<D>();
+  constexpr int BC = kBC8;
+  constexpr int NKB = BC / 32;       // 32-key score blocks per tile
+  constexpr int NKS = D / 64;        // k-steps of the score product
+  constexpr int NDB = D / 32;        // 32-dim output blocks
+  constexpr int P8 = f8_pitch<D>();
+  using Plan = DmaPlanBytes<D, BC, P8, kWaves>;
+  constexpr int TB = Plan::BYTES;
+  constexpr int KMIN = Plan::NI / kWaves;   // may be 0 (small tiles): such waves issue no DMA
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NS * TB];
   __shared__ float red[kWaves];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const int H = p.H, N = p.N;
   const int nqt = (N + kBR - 1) / kBR;
@@ -180,30 +216,33 @@ __global__ __launch_bounds__(256) void fwd_fp8_kernel(Fp8FwdParams p) {
   const int bh = work / nqt;
   const int h = bh % H, b = bh / H;
   const int qt = CAUSAL ? nqt - 1 - qi : qi;
-  const int q0 = qt * kBR + wave * kQW;
+  const int q0 = qt * kBR + wave * kQW8;
   const int qrow = q0 + l32;
 
   const uint32_t row_bytes = (uint32_t)H * D;
   const size_t head_off = ((size_t)b * N * H + h) * D;
   const uint32_t nrec = (uint32_t)N * row_bytes - (uint32_t)h * D;
   const auto rq = make_rsrc(p.q8 + head_off, nrec);
-  const auto rk = make_rsrc(p.k8 + head_off, nrec);
-  const auto rv = make_rsrc(p.v8 + head_off, nrec);
   const uint32_t orow = (uint32_t)H * D * 2;
   const auto ro = make_rsrc((char*)p.o + head_off * 2, (uint32_t)N * orow - (uint32_t)h * D * 2);
   const float* dq_h = p.dq + ((size_t)b * H + h) * nblk;
   const float* dk_h = p.dk + ((size_t)b * H + h) * nblk;
   const float* dv_h = p.dv + ((size_t)b * H + h) * nblk;
+  const auto rdk = make_rsrc(dk_h, (uint32_t)nblk * 4);
+  const auto rdv = make_rsrc(dv_h, (uint32_t)nblk * 4);
 
-  // largest V descale of the head
+  // largest V descale of the head (before any DMA is in flight)
   float dvm = 0.f;
-  for (int i = tid; i < nblk; i += 256) dvm = fmaxf(dvm, dv_h[i]);
+  for (int i = tid; i < nblk; i += 64 * kWaves) dvm = fmaxf(dvm, dv_h[i]);
 #pragma unroll
   for (int m = 32; m > 0; m >>= 1) dvm = fmaxf(dvm, __shfl_xor(dvm, m));
   if (lane == 0) red[wave] = dvm;
   __syncthreads();
-  dvm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  dvm = red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) dvm = fmaxf(dvm, red[w]);
 
+  // Q^T operand: lane holds query q0 + l32, dims 64*ks + 32*hf .. +31.
   i32x8 qreg[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
@@ -211,175 +250,237 @@ __global__ __launch_bounds__(256) void fwd_fp8_kernel(Fp8FwdParams p) {
     const u32x4 c = buf_load16(rq, (uint32_t)qrow * row_bytes + 64 * ks + 32 * hf + 16);
     qreg[ks] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
   }
-  const float dq_row = qrow < N ? dq_h[qrow >> 6] : 1.0f;
-  const float cq = p.c * dq_row;
+  const float cq = p.c * (qrow < N ? dq_h[qrow >> 6] : 1.0f);
 
   const int kend = CAUSAL ? min(N, (qt + 1) * kBR) : N;
   const int nkt = (kend + BC - 1) / BC;
+  const int nkt_w = q0 >= N ? 0 : CAUSAL ? min(nkt, (q0 + kQW8 - 1) / BC + 1) : nkt;
+  auto is_edge = [&](int j) { const int k0 = j * BC; return (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0); };
+  // Stage offsets pass through readfirstlane: opaque to loop strength reduction.
+  auto kst = [&](int j) { return smem + __builtin_amdgcn_readfirstlane((j % NS) * TB); };
+  auto vst = [&](int j) { return smem + NS * TB + __builtin_amdgcn_readfirstlane((j % NS) * TB); };
+  uint32_t voff[Plan::NPW];
+  dma_init<Plan, kWaves>(voff, row_bytes, wave, lane);
+  const char* kbase = (const char*)p.k8 + head_off;
+  const char* vbase = (const char*)p.v8 + head_off;
+  auto dma_k = [&](int t) { dma_issue<Plan, kWaves>(voff, kst(t), kbase, t * BC, row_bytes, nrec, wave); };
+  auto dma_v = [&](int t) { dma_issue<Plan, kWaves>(voff, vst(t), vbase, t * BC, row_bytes, nrec, wave); };
 
-  u32x4 kreg[KIT];
-  u32x4 vreg[VIT][4];
-  auto load_tile = [&](int k0) {
+  // DMA schedule as in the bf16 forward: the prologue requests K(0), then V(t), K(t+1) for
+  // t = 0 .. NS-2; iteration j requests V(j+NS-1), K(j+NS); before iteration j, K(j+1) and
+  // V(j) must have landed.
+  const int n_w = KMIN + (wave < Plan::NI % kWaves ? 1 : 0);   // this wave's DMA share per tile
+  constexpr int KEEP_MAX = (NS - 2) * 2 * (KMIN + 1);
+  auto wait_before = [&](int j) {
+    int keep = 0;
 #pragma unroll
-    for (int it = 0; it < KIT; ++it) {
-      const int i = tid + 256 * it, c16 = i % (D / 16), kr = i / (D / 16);
-      kreg[it] = buf_load16(rk, (uint32_t)(k0 + kr) * row_bytes + c16 * 16);
-    }
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const int i = tid + 256 * it;
-      if (VITEMS % 256 == 0 || i < VITEMS) {
-        const int c16 = i % (D / 16), m = i / (D / 16);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vreg[it][r] = buf_load16(rv, (uint32_t)(k0 + 4 * m + r) * row_bytes + c16 * 16);
-      }
-    }
+    for (int t = 1; t <= NS - 2; ++t) keep += (j + t < nkt ? n_w : 0) + (j + t + 1 < nkt ? n_w : 0);
+    wait_dma_keep_rt<KEEP_MAX>(keep);
   };
-  auto store_tile = [&](int stage) {
-    char* ks = smem + stage * STAGE;
-    char* vs = ks + KBYTES;
-#pragma unroll
-    for (int it = 0; it < KIT; ++it) {
-      const int i = tid + 256 * it, c16 = i % (D / 16), kr = i / (D / 16);
-      *(u32x4*)(ks + kr * KP + c16 * 16) = kreg[it];
-    }
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const int i = tid + 256 * it;
-      if (VITEMS % 256 == 0 || i < VITEMS) {
-        const int c16 = i % (D / 16), m = i / (D / 16);
-        const int pos = (4 * m & ~63) + fp8_vpos(4 * m);   // 64-key chunk + position inside it
-        const int g = pos >> 4, boff = pos & 15;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t a0 = vreg[it][0][w], a1 = vreg[it][1][w], a2 = vreg[it][2][w], a3 = vreg[it][3][w];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int d = c16 * 16 + 4 * w + j;
-            const uint32_t x = ((a0 >> (8 * j)) & 0xffu) | (((a1 >> (8 * j)) & 0xffu) << 8) |
-                               (((a2 >> (8 * j)) & 0xffu) << 16) | (((a3 >> (8 * j)) & 0xffu) << 24);
-            *(uint32_t*)(vs + d * VP + ((g ^ fp8_vswz(d)) & 7) * 16 + boff) = x;
-          }
-        }
-      }
-    }
+  // per-tile descale factors, loaded one tile ahead (before that iteration's DMA batch)
+  auto load_desc = [&](int t, float& dk, float& dv) {
+    dk = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdk, (uint32_t)t * 4, 0, 0));
+    dv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdv, (uint32_t)t * 4, 0, 0));
   };
+  float dk_c, dv_c;   // descales of the tile the next iteration exponentiates
+  load_desc(0, dk_c, dv_c);
+
+  dma_k(0);
+#pragma unroll
+  for (int t = 0; t <= NS - 2; ++t) {
+    if (t < nkt) dma_v(t);
+    if (t + 1 < nkt) dma_k(t + 1);
+  }
 
   f32x16 oacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
-  const bool wave_live = q0 < N;
+  const int k_lane = k8_lane_off<P8>(lane), v_lane = vt8_lane_off<P8>(lane);
 
-  load_tile(0);
-  store_tile(0);
+  wait_before(0);
   __syncthreads();
 
-  for (int j = 0; j < nkt; ++j) {
-    const int k0 = j * BC;
-    const bool more = j + 1 < nkt;
-    if (more) load_tile(k0 + BC);
-    const char* ks = smem + (j & 1) * STAGE;
-    const char* vs = ks + KBYTES;
-    const bool skip = !wave_live || (CAUSAL && k0 > q0 + kQW - 1);
-    if (!skip) {
-      f32x16 s[NKB];
+  auto tile_scores = [&](f32x16 (&sc)[NKB], const char* kl) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        s[kb] = f32x16{};
+    for (int kb = 0; kb < NKB; ++kb) {
+      sc[kb] = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < NKS; ++kk) {
-          const char* kr = ks + (kb * 32 + l32) * KP + 64 * kk + 32 * hf;
-          const u32x4 a = *(const u32x4*)kr;
-          const u32x4 c = *(const u32x4*)(kr + 16);
-          const i32x8 av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
-          s[kb] = mfma_f8(av, qreg[kk], s[kb]);
-        }
+      for (int ks = 0; ks < NKS; ++ks) sc[kb] = mfma_f8(lds_k8<P8>(kl, kb, ks), qreg[ks], sc[kb]);
+    }
+  };
+  auto tile_mask = [&](f32x16 (&sc)[NKB], int k0) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (key >= N || (CAUSAL && key > qrow)) sc[kb][r] = -INFINITY;
       }
-      float coef[NC2], bias[NC2], winv[NC2];
+  };
+  auto tile_max = [&](const f32x16 (&sc)[NKB], float coef) {
+    float mx = -INFINITY;
 #pragma unroll
-      for (int c2 = 0; c2 < NC2; ++c2) {
-        const int blk = min((k0 >> 6) + c2, nblk - 1);
-        const float dv = dv_h[blk];
-        coef[c2] = cq * dk_h[blk];
-        const float wgt = kPScale * (dv / dvm);
-        bias[c2] = fast_log2(wgt);
-        winv[c2] = 1.0f / wgt;
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+    mx = xhalf_max(mx);
+    return mx == -INFINITY ? -INFINITY : mx * coef;
+  };
+
+  // prologue: scores and maximum of tile 0
+  f32x16 sc[NKB], sn[NKB];
+  float mx_next = -INFINITY;
+  float coef_c = cq * dk_c;   // coefficient of the tile held in sc
+  if (nkt_w > 0) {
+    tile_scores(sc, kst(0) + k_lane);
+    if (is_edge(0)) tile_mask(sc, 0);
+    mx_next = tile_max(sc, coef_c);
+  }
+  // the first prefetch overwrites the stage of K(0), which the prologue just read
+  __syncthreads();
+
+  auto prefetch = [&](int j) {
+    if (j + NS - 1 < nkt) dma_v(j + NS - 1);
+    if (j + NS < nkt) dma_k(j + NS);
+  };
+  auto end_tile = [&](int j) {
+    wait_before(j + 1);
+    __syncthreads();
+  };
+  auto rescale = [&]() {
+    const float m_cand = fmaxf(m_run, mx_next);
+    if (__builtin_amdgcn_ballot_w64(m_cand > m_run + kTau8)) {
+      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_cand);
+      m_run = m_cand;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < NDB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+    }
+  };
+
+  // Interior tiles, pipelined with the instruction order written out. Block 1: one S(j+1)
+  // MFMA per step, EPS exponentials of tile j under each, packed to fp8 four at a time.
+  // Block 2: one P~(j)V(j) MFMA per step (one per 32-dim output block), the row-sum terms
+  // of tile j and the row maximum of tile j+1 under it.
+  constexpr int S1 = NKB * NKS;
+  constexpr int S2 = NDB;
+  constexpr int EPS = 16 * NKB / S1;
+  constexpr int MPS = 16 * NKB / S2;
+  constexpr int PF = 2;
+  static_assert(EPS * S1 == 16 * NKB && MPS * S2 == 16 * NKB && EPS % 4 == 0 && MPS % 2 == 0, "step split");
+  float dk_n, dv_n;
+  auto fast_iter = [&](int jj, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) {
+    load_desc(jj + 1 < nkt ? jj + 1 : jj, dk_n, dv_n);
+    prefetch(jj);
+    rescale();
+    const float wgt = kPScale * (dv_c / dvm);
+    const float bias = fast_log2(wgt) - m_run;
+    const char* kn = kst(jj + 1) + k_lane;
+    const char* vc = vst(jj) + v_lane;
+    i32x8 pk;
+    i32x8 kop[S1];
+    float e[16 * NKB];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < PF && t < S1; ++t) kop[t] = lds_k8<P8>(kn, t % NKB, t / NKB);
+#pragma unroll
+    for (int t = 0; t < S1; ++t) {
+      if (t + PF < S1) kop[t + PF] = lds_k8<P8>(kn, (t + PF) % NKB, (t + PF) / NKB);
+      const int kb = t % NKB, ks = t / NKB;
+      nxt[kb] = mfma_f8(kop[t], qreg[ks], ks == 0 ? f32x16{} : nxt[kb]);
+#pragma unroll
+      for (int u = 0; u < EPS; ++u) {
+        const int i = EPS * t + u;
+        e[i] = fast_exp2(fmaf(cur[i >> 4][i & 15], coef_c, bias));
+        if ((i & 3) == 3) pk[i >> 2] = (int)cvt4_fp8(e[i - 3], e[i - 2], e[i - 1], e[i]);
       }
-      const bool edge = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0);
-      if (edge) {
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const float coef_n = cq * dk_n;
+    i32x8 vop[S2];
+    float mx = -INFINITY, psum = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+    for (int t = 0; t < PF && t < S2; ++t) vop[t] = lds_vt8<P8>(vc, t);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
-          }
+    for (int t = 0; t < S2; ++t) {
+      if (t + PF < S2) vop[t + PF] = lds_vt8<P8>(vc, t + PF);
+      oacc[t] = mfma_f8(vop[t], pk, oacc[t]);
+#pragma unroll
+      for (int u = 0; u < MPS; u += 2) {
+        const int i2 = MPS * t + u;
+        psum += e[i2];
+        psum += e[i2 + 1];
+        mx = fmaxf(mx, fmaxf(nxt[i2 >> 4][i2 & 15], nxt[(i2 + 1) >> 4][(i2 + 1) & 15]));
       }
-      float mt = -INFINITY;
+      pin(psum);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run = fmaf(psum, 1.0f / wgt, l_run);
+    mx = xhalf_max(mx);
+    mx_next = mx * coef_n;
+    coef_c = coef_n;
+    dk_c = dk_n;
+    dv_c = dv_n;
+    end_tile(jj);
+  };
+  int j = 0;
+  for (; j + 2 < nkt_w && !is_edge(j + 2); j += 2) {
+    fast_iter(j, sc, sn);
+    fast_iter(j + 1, sn, sc);
+  }
+  if (j + 1 < nkt_w && !is_edge(j + 1)) {
+    fast_iter(j, sc, sn);
 #pragma unroll
-      for (int c2 = 0; c2 < NC2; ++c2) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 2 * c2; kb < 2 * c2 + 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mt = fmaxf(mt, mx == -INFINITY ? -INFINITY : mx * coef[c2]);
-      }
-      mt = xhalf_max(mt);
-      const float m_cand = fmaxf(m_run, mt);
-      if (__builtin_amdgcn_ballot_w64(m_cand > m_run + kTau8)) {
-        const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_cand);
-        m_run = m_cand;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < NDB; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-      }
+    for (int kb = 0; kb < NKB; ++kb) sc[kb] = sn[kb];
+    ++j;
+  }
+  // Remaining tiles, in order: masked tiles and the tail of the key range (waves with
+  // nothing left to compute only take part in the ring bookkeeping).
+  for (; j < nkt; ++j) {
+    load_desc(j + 1 < nkt ? j + 1 : j, dk_n, dv_n);
+    prefetch(j);
+    if (j < nkt_w) {
+      rescale();
       const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      i32x8 pk[NC2];
+      const float wgt = kPScale * (dv_c / dvm);
+      const float bias = fast_log2(wgt) - m_use;
+      const bool edge = is_edge(j);
+      i32x8 pk;
+      float psum = 0.f;
 #pragma unroll
-      for (int c2 = 0; c2 < NC2; ++c2) {
-        const float bb = bias[c2] - m_use;
-        float psum = 0.f;
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int kb = 2 * c2; kb < 2 * c2 + 2; ++kb)
+        for (int r4 = 0; r4 < 4; ++r4) {
+          float e4[4];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float e = fast_exp2(fmaf(s[kb][r], coef[c2], bb));
-            if (edge) e = (s[kb][r] == -INFINITY) ? 0.f : e;
-            s[kb][r] = e;
-            psum += e;
+          for (int u = 0; u < 4; ++u) {
+            const float x = sc[kb][4 * r4 + u];
+            e4[u] = fast_exp2(fmaf(x, coef_c, bias));
+            if (edge && x == -INFINITY) e4[u] = 0.f;
+            psum += e4[u];
           }
-        l_run = fmaf(psum, winv[c2], l_run);
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const f32x16& sv = s[2 * c2 + (w >> 2)];
-          const int r0 = 4 * (w & 3);
-          pk[c2][w] = (int)cvt4_fp8(sv[r0], sv[r0 + 1], sv[r0 + 2], sv[r0 + 3]);
+          pk[4 * kb + r4] = (int)cvt4_fp8(e4[0], e4[1], e4[2], e4[3]);
         }
-      }
+      l_run = fmaf(psum, 1.0f / wgt, l_run);
+      const char* vc = vst(j) + v_lane;
 #pragma unroll
-      for (int i = 0; i < NDB; ++i) {
-        const int d = i * 32 + l32;
-        const char* vrow = vs + d * VP;
-        const int sw = fp8_vswz(d);
-#pragma unroll
-        for (int c2 = 0; c2 < NC2; ++c2) {
-          const int g0 = 4 * c2 + 2 * hf;
-          const u32x4 a = *(const u32x4*)(vrow + ((g0 ^ sw) & 7) * 16);
-          const u32x4 c = *(const u32x4*)(vrow + (((g0 + 1) ^ sw) & 7) * 16);
-          const i32x8 av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
-          oacc[i] = mfma_f8(av, pk[c2], oacc[i]);
-        }
+      for (int i = 0; i < NDB; ++i) oacc[i] = mfma_f8(lds_vt8<P8>(vc, i), pk, oacc[i]);
+      if (j + 1 < nkt_w) {
+        tile_scores(sc, kst(j + 1) + k_lane);
+        if (is_edge(j + 1)) tile_mask(sc, (j + 1) * BC);
+        mx_next = tile_max(sc, cq * dk_n);
       }
     }
-    if (more) store_tile((j + 1) & 1);
-    __syncthreads();
+    coef_c = cq * dk_n;
+    dk_c = dk_n;
+    dv_c = dv_n;
+    end_tile(j);
   }
 
-  if (wave_live) {
+  if (nkt_w > 0) {
     const float l_tot = xhalf_sum(l_run);
     const float fac = dvm / kPScale / l_tot;
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
@@ -405,8 +506,9 @@ hipError_t launch_q(const Fp8QuantParams& p, hipStream_t s) {
 
 template <bool OUT_BF16, int D, bool CAUSAL>
 hipError_t launch_f(const Fp8FwdParams& p, hipStream_t s) {
-  const int nqt = (p.N + kBR - 1) / kBR;
-  hipLaunchKernelGGL((fwd_fp8_kernel<OUT_BF16, D, CAUSAL>), dim3((unsigned)(p.B * p.H * nqt)), dim3(256), 0, s, p);
+  const int nqt = (p.N + fp8_rows<D>() - 1) / fp8_rows<D>();
+  hipLaunchKernelGGL((fwd_fp8_kernel<OUT_BF16, D, CAUSAL>), dim3((unsigned)(p.B * p.H * nqt)),
+                     dim3(64 * Fp8Cfg<D>::WAVES), 0, s, p);
   return hipGetLastError();
 }
 

@@ -29,18 +29,22 @@ typedef __attribute__((address_space(3))) void lds_void;
 template <int D> __host__ __device__ constexpr int k_pitch() { return 2 * D + 16; }
 template <int D> __host__ __device__ constexpr int v_pitch() { return 2 * D + 64; }
 
-// DMA plan of a ROWS x D tile with a padded row pitch (constants only; the per-lane offsets
-// live in a plain uint32_t[NPW] register array, filled by dma_init and used by dma_issue).
-template <int D, int ROWS, int PITCH, int NWAVES>
-struct DmaPlan {
+// DMA plan of a ROWS x RB-byte tile with a padded row pitch (constants only; the per-lane
+// offsets live in a plain uint32_t[NPW] register array, filled by dma_init and used by
+// dma_issue).
+template <int RB, int ROWS, int PITCH, int NWAVES>
+struct DmaPlanBytes {
   static constexpr int CPRP = PITCH / 16;             // 16-byte slots per padded row
-  static constexpr int CPR = 2 * D / 16;              // data chunks per row
+  static constexpr int CPR = RB / 16;                 // data chunks per row
   static constexpr int SLOTS = ROWS * CPRP;
   static constexpr int NI = (SLOTS + 63) / 64;        // wave instructions per tile
   static constexpr int NPW = (NI + NWAVES - 1) / NWAVES;
   static constexpr int BYTES = NI * 1024;             // LDS taken (the last instruction may overhang the tile)
-  static_assert(PITCH % 16 == 0, "pitch must be whole 16-byte slots");
+  static_assert(PITCH % 16 == 0 && RB % 16 == 0, "pitch and row must be whole 16-byte slots");
 };
+// 16-bit elements, D per row.
+template <int D, int ROWS, int PITCH, int NWAVES>
+using DmaPlan = DmaPlanBytes<2 * D, ROWS, PITCH, NWAVES>;
 
 template <class Plan, int NWAVES>
 __device__ __forceinline__ void dma_init(uint32_t* voff, uint32_t row_bytes, int wave, int lane) {
