@@ -115,7 +115,10 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
   constexpr int BKV = kWaves * 32;
-  constexpr int QP = rt_pitch<D>();
+  // d <= 128: unpadded Q/dO tiles with the chunk swizzle (conflict-free row and transpose
+  // reads); d = 256 (no registers to spare for the read offsets): padded pitch 2d + 48.
+  constexpr int SWZ = D <= 128 ? D : 0;
+  constexpr int QP = SWZ ? 2 * D : rt_pitch<D>();
   using QPlan = DmaPlan<D, BQ, QP, kWaves>;
   constexpr int TB = QPlan::BYTES;
   constexpr int OFF_DO = TB, OFF_L = 2 * TB, OFF_D = 2 * TB + BQ * 4;
@@ -149,7 +152,7 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
   const int nqt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? (kt * BKV) / BQ : 0;
   uint32_t qvoff[QPlan::NPW];
-  dma_init<QPlan, kWaves>(qvoff, row_bytes, wave, lane);
+  dma_init<QPlan, kWaves, SWZ>(qvoff, row_bytes, wave, lane);
   float lval = 0.f, dval = 0.f;   // L (log2 domain) and D of query row (tile start + tid), tid < BQ
   auto load_ld = [&](int qt) {
     if (tid < BQ) {
@@ -193,6 +196,8 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
   const bool wave_live = k0w < N;
   const float c = p.c;
   const int row_q = row_lane_off<QP>(lane), tr_q = tr_lane_off<QP>(lane);
+  int srow[SWZ ? D / 16 : 1], str_[2][SWZ ? D / 32 : 1];
+  if constexpr (SWZ != 0) swz_offsets<D>(lane, srow, str_);
 
   wait_dma();
   __syncthreads();
@@ -246,10 +251,15 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
     auto operand = [&](int g) -> u32x4 {
       if (g < NQB * SC) {
         const int qb = g / SC, t = g % SC, kk = t >> 1;
+        if constexpr (SWZ != 0) return lds_read16(st + ((t & 1) ? OFF_DO : 0) + srow[kk] + qb * 32 * QP);
         return (t & 1) ? lds_row<QP>(dr, qb, kk) : lds_row<QP>(qr, qb, kk);
       }
       const int qb = (g - NQB * SC) / UP, t = (g - NQB * SC) % UP;
       const int cc = 2 * qb + t / (2 * NDB), i = (t >> 1) % NDB;
+      if constexpr (SWZ != 0) {
+        const char* base = st + ((t & 1) ? 0 : OFF_DO) + cc * 16 * QP;
+        return lds_tr_pair(base + str_[0][i], base + str_[1][i]);
+      }
       return (t & 1) ? lds_tr<QP>(qtr, cc, i) : lds_tr<QP>(dtr, cc, i);
     };
     auto mfma_step = [&](int g, const u32x4& op) {
@@ -380,7 +390,10 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(BwdParams p)
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
   constexpr int BR = kWaves * 32;
-  constexpr int KP = rt_pitch<D>(), VP = k_pitch<D>();
+  // K tiles are read both as rows and transposed: unpadded with the chunk swizzle at d <= 128
+  // (padded pitch 2d + 48 at d = 256); V tiles only as rows.
+  constexpr int SWZ = D <= 128 ? D : 0;
+  constexpr int KP = SWZ ? 2 * D : rt_pitch<D>(), VP = k_pitch<D>();
   using KPlan = DmaPlan<D, BC, KP, kWaves>;
   using VPlan = DmaPlan<D, BC, VP, kWaves>;
   constexpr int KB = KPlan::BYTES, VB = VPlan::BYTES, STAGE = KB + VB;
@@ -412,7 +425,7 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(BwdParams p)
   const int nkt = (kend + BC - 1) / BC;
   const int nkt_w = q0 >= N ? 0 : CAUSAL ? min(nkt, (q0 + 31) / BC + 1) : nkt;
   uint32_t kvoff[KPlan::NPW], vvoff[VPlan::NPW];
-  dma_init<KPlan, kWaves>(kvoff, row_bytes, wave, lane);
+  dma_init<KPlan, kWaves, SWZ>(kvoff, row_bytes, wave, lane);
   dma_init<VPlan, kWaves>(vvoff, row_bytes, wave, lane);
   auto fetch = [&](int j) {
     char* st = smem + (j & 1) * STAGE;
@@ -436,6 +449,16 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(BwdParams p)
   for (int i = 0; i < NDB; ++i) dqacc[i] = f32x16{};
   const float c = p.c;
   const int row_k = row_lane_off<KP>(lane), tr_k = tr_lane_off<KP>(lane), row_v = row_lane_off<VP>(lane);
+  int srow[SWZ ? D / 16 : 1], str_[2][SWZ ? D / 32 : 1];
+  if constexpr (SWZ != 0) swz_offsets<D>(lane, srow, str_);
+  auto k_row = [&](const char* st, int kb, int kk) -> u32x4 {
+    if constexpr (SWZ != 0) return lds_read16(st + srow[kk] + kb * 32 * KP);
+    return lds_row<KP>(st + row_k, kb, kk);
+  };
+  auto k_tr = [&](const char* st, int c, int i) -> u32x4 {
+    if constexpr (SWZ != 0) return lds_tr_pair(st + c * 16 * KP + str_[0][i], st + c * 16 * KP + str_[1][i]);
+    return lds_tr<KP>(st + tr_k, c, i);
+  };
 
   wait_dma();
   __syncthreads();
@@ -446,8 +469,6 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(BwdParams p)
   auto tile = [&](int j, auto edge_tag) {
     constexpr bool EDGE = decltype(edge_tag)::value;
     const char* st = smem + (j & 1) * STAGE;
-    const char* kr = st + row_k;
-    const char* kt = st + tr_k;
     const char* vr = st + KB + row_v;
     const int k0 = j * BC;
     f32x16 s[NKB], dp[NKB];
@@ -455,10 +476,10 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(BwdParams p)
     // phase 1: S^T = K Q^T
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < PF; ++t) op[t] = lds_row<KP>(kr, t % NKB, t / NKB);
+    for (int t = 0; t < PF; ++t) op[t] = k_row(st, t % NKB, t / NKB);
 #pragma unroll
     for (int t = 0; t < S1; ++t) {
-      if (t + PF < S1) op[t + PF] = lds_row<KP>(kr, (t + PF) % NKB, (t + PF) / NKB);
+      if (t + PF < S1) op[t + PF] = k_row(st, (t + PF) % NKB, (t + PF) / NKB);
       const int kb = t % NKB, kk = t / NKB;
       s[kb] = mfma32x16<BF16>(op[t], qreg[kk], kk == 0 ? f32x16{} : s[kb]);
       __builtin_amdgcn_sched_barrier(0);
@@ -494,12 +515,12 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(BwdParams p)
     };
     u32x4 kop[BC / 16 * NDB];
 #pragma unroll
-    for (int t = 0; t < PF; ++t) kop[t] = lds_tr<KP>(kt, t / NDB, t % NDB);
+    for (int t = 0; t < PF; ++t) kop[t] = k_tr(st, t / NDB, t % NDB);
     ds_chunk(0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < BC / 16 * NDB; ++t) {
-      if (t + PF < BC / 16 * NDB) kop[t + PF] = lds_tr<KP>(kt, (t + PF) / NDB, (t + PF) % NDB);
+      if (t + PF < BC / 16 * NDB) kop[t + PF] = k_tr(st, (t + PF) / NDB, (t + PF) % NDB);
       const int cc = t / NDB, i = t % NDB;
       dqacc[i] = mfma32x16<BF16>(kop[t], dspk[cc], dqacc[i]);
       if (i == NDB - 1 && cc + 1 < BC / 16) ds_chunk(cc + 1);

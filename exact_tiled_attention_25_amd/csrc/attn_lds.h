@@ -46,14 +46,27 @@ struct DmaPlanBytes {
 template <int D, int ROWS, int PITCH, int NWAVES>
 using DmaPlan = DmaPlanBytes<2 * D, ROWS, PITCH, NWAVES>;
 
-template <class Plan, int NWAVES>
+// Chunk swizzle of an unpadded 16-bit tile (pitch 2D bytes): logical 16-byte chunk c of row
+// r is stored at chunk c ^ swz<D>(r). It makes both read patterns conflict-free on the
+// 64-bank LDS: row reads (a 16-lane pass: 16 consecutive rows, one chunk) and transpose
+// reads (a 32-lane pass: 4 consecutive rows from a multiple of 4, 4 chunks from a multiple
+// of 4). d = 128 (256-byte rows, every row starts on bank 0): swz = 4*(r%4) + (r/4)%4,
+// a bijection on r%16 whose bits 2-3 move with r%4. d = 64 (128-byte rows alternate bank
+// halves): swz = 4*((r/2)%2) + (r/4)%4. SWZ = 0 selects no swizzle.
+template <int SWZ>
+__host__ __device__ constexpr int swz(int r) {
+  return SWZ == 0 ? 0 : SWZ == 64 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) : (((r & 3) << 2) | ((r >> 2) & 3));
+}
+
+template <class Plan, int NWAVES, int SWZ = 0>
 __device__ __forceinline__ void dma_init(uint32_t* voff, uint32_t row_bytes, int wave, int lane) {
 #pragma unroll
   for (int t = 0; t < Plan::NPW; ++t) {
     const int blk = wave + NWAVES * t;
     const int g = blk * 64 + lane;
     const int r = g / Plan::CPRP, cp = g % Plan::CPRP;
-    voff[t] = (blk < Plan::NI && g < Plan::SLOTS && cp < Plan::CPR) ? (uint32_t)r * row_bytes + cp * 16 : 0x80000000u;
+    voff[t] = (blk < Plan::NI && g < Plan::SLOTS && cp < Plan::CPR) ? (uint32_t)r * row_bytes + (cp ^ swz<SWZ>(r)) * 16
+                                                                     : 0x80000000u;
   }
 }
 
@@ -101,6 +114,33 @@ __device__ __forceinline__ u32x4 lds_tr(const char* lane_base, int c, int i) {
 }
 // Pitch for tiles read both ways: rows conflict-free, transposed reads 2-way.
 template <int D> __host__ __device__ constexpr int rt_pitch() { return 2 * D + 48; }
+
+// Reads of a swizzled tile (pitch 2D) through per-lane offsets computed once per kernel.
+// Row reads: lane l, 16-dim step ks, row block blk -> rows 32*blk + l%32, dims 16*ks + 8*(l/32)
+// at tile + row_off[ks] + blk*32*2D. Transpose reads (the same operand as lds_tr): chunk-row
+// block c, output block i -> tile + tr_off[0][i] + c*16*2D and tile + tr_off[1][i] + c*16*2D.
+template <int D>
+__device__ __forceinline__ void swz_offsets(int lane, int (&row_off)[D / 16], int (&tr_off)[2][D / 32]) {
+  constexpr int RB = 2 * D;
+  const int hf = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) row_off[ks] = (lane & 31) * RB + 16 * ((2 * ks + hf) ^ swz<D>(lane & 15));
+  const int i16 = lane & 15, g1 = (lane >> 4) & 1;
+  const int lo = 2 * g1 + ((i16 & 3) >> 1);   // chunk within the 4-chunk (32-dim) group
+#pragma unroll
+  for (int sec = 0; sec < 2; ++sec) {
+    const int r = 4 * hf + (i16 >> 2) + 8 * sec;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) tr_off[sec][i] = r * RB + 16 * ((4 * i + lo) ^ swz<D>(r)) + 8 * (i16 & 1);
+  }
+}
+__device__ __forceinline__ u32x4 lds_read16(const char* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ u32x4 lds_tr_pair(const char* p0, const char* p1) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p0);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p1);
+  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  return u32x4{ua[0], ua[1], ub[0], ub[1]};
+}
 
 // Forward-kernel aliases: K tiles are read as rows, V tiles transposed.
 template <int D>
