@@ -163,12 +163,12 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
   };
   auto fetch = [&](int qt, int stage) {
     char* st = smem + stage * STAGE;
-    dma_issue<QPlan, kWaves>(qvoff, st, qbase, qt * BQ, row_bytes, nrec, wave);
-    dma_issue<QPlan, kWaves>(qvoff, st + OFF_DO, dobase, qt * BQ, row_bytes, nrec, wave);
     if (tid < BQ) {
       ((float*)(st + OFF_L))[tid] = lval;
       ((float*)(st + OFF_D))[tid] = dval;
     }
+    dma_issue<QPlan, kWaves>(qvoff, st, qbase, qt * BQ, row_bytes, nrec, wave);
+    dma_issue<QPlan, kWaves>(qvoff, st + OFF_DO, dobase, qt * BQ, row_bytes, nrec, wave);
   };
   if (qt0 < nqt) {
     load_ld(qt0);
@@ -181,6 +181,11 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
   for (int ks = 0; ks < NKS; ++ks) {
     kreg[ks] = buf_load16(rk, (uint32_t)key * row_bytes + (16 * ks + 8 * hf) * 2);
     vreg[ks] = buf_load16(rv, (uint32_t)key * row_bytes + (16 * ks + 8 * hf) * 2);
+  }
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {   // waited for here, not inside the tile loop
+    settle(kreg[ks]);
+    settle(vreg[ks]);
   }
   // One wave per SIMD (512 registers): every MFMA accumulator (dK, dV for the whole kernel,
   // S and dP per block) lives in AGPRs; K, V and everything the VALU writes in VGPRs.
@@ -443,6 +448,13 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(BwdParams p)
   const bool row_ok = qrow < N;
   const float lse2 = row_ok ? p.lse[((size_t)b * H + h) * N + qrow] * kLog2e : 0.f;
   const float drow = row_ok ? p.delta[((size_t)b * H + h) * N + qrow] : 0.f;
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {   // waited for here, not inside the tile loop
+    settle(qreg[ks]);
+    settle(doreg[ks]);
+  }
+  settle(lse2);
+  settle(drow);
 
   f32x16 dqacc[NDB];
 #pragma unroll

@@ -100,6 +100,21 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
 // cannot be sunk past later scheduling fences (used to keep VALU work under the MFMAs it
 // was placed beside).
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+// Makes the compiler wait here for a register loaded from memory. Without it the wait is
+// placed at the register's first use; when that use sits inside a loop (the first use
+// before the loop being conditional), every iteration executes the wait, and once the loop
+// has DMA in flight a vmcnt wait there waits for that DMA as well.
+// (The host compilation pass checks asm constraints against x86, where "v" on a 256-bit
+// vector is invalid; the statement only matters in the device pass.)
+template <class T>
+__device__ __forceinline__ void settle(const T& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" ::"v"(x));
+#else
+  (void)x;
+#endif
+}
+
 // Ties an MFMA accumulator to the accumulation register file (AGPRs). Accumulators that
 // live across a whole loop and are only touched by MFMAs belong there; without the hint
 // the allocator may park them in VGPRs and copy them over before every MFMA.

@@ -251,6 +251,9 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
     qreg[ks] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
   }
   const float cq = p.c * (qrow < N ? dq_h[qrow >> 6] : 1.0f);
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) settle(qreg[ks]);   // waited for here, not inside the tile loop
+  settle(cq);
 
   const int kend = CAUSAL ? min(N, (qt + 1) * kBR) : N;
   const int nkt = (kend + BC - 1) / BC;

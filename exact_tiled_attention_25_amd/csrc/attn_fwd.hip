@@ -184,6 +184,8 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::WAVES, 1) void fwd_kernel(FwdParams
   u32x4 qreg[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) qreg[ks] = buf_load16(rq, (uint32_t)qrow * row_bytes + (16 * ks + 8 * hf) * 2);
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) settle(qreg[ks]);   // before any DMA is in flight
 
   // Prologue requests K(0), then the pairs V(t), K(t+1) for t = 0 .. NS-2; loop iteration
   // j requests the pair V(j+NS-1), K(j+NS). Before iteration j (and before the loop, j = 0)
