@@ -100,6 +100,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
 // cannot be sunk past later scheduling fences (used to keep VALU work under the MFMAs it
 // was placed beside).
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
 // Makes the compiler wait here for a register loaded from memory. Without it the wait is
 // placed at the register's first use; when that use sits inside a loop (the first use
 // before the loop being conditional), every iteration executes the wait, and once the loop

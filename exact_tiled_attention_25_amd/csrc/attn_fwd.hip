@@ -8,9 +8,12 @@
 //
 // gfx950 design (the Hopper producer/consumer, TMA and WGMMA machinery is prior art only):
 //  * d = 64, 128: 8 waves x 32 query rows = 256 rows per workgroup, one workgroup per CU
-//    (two waves per SIMD, so one wave's softmax runs while the other's MFMAs do), sharing
-//    one three-stage K/V ring; key tiles of BC = 64. d = 256 needs more than 256 registers:
-//    4 waves (one per SIMD) and a two-stage ring.
+//    (two waves per SIMD), sharing a three-stage K ring and a four-stage V ring; key tiles
+//    of BC = 64. Ping-pong between the two waves of a SIMD (same page, Deep Dive, "Ping-pong
+//    scheduling"): the second wave takes each tile's barrier between its
+//    score block and its P~V block, so on every SIMD one wave's exponentials run beside
+//    the other wave's P~V MFMAs; the extra V stage covers the late reads. d = 256 needs
+//    more than 256 registers: 4 waves (one per SIMD) and two-stage rings.
 //  * K and V tiles go from HBM straight into the LDS ring by DMA (buffer_load_dwordx4 ...
 //    lds) with no register staging; with NS stages each tile is requested NS-2 loop
 //    iterations before the one whose end must see it landed, so the DMA latency hides under
@@ -43,10 +46,11 @@ namespace {
 
 template <int D> struct FwdCfg;
 // BC: keys per tile; WAVES: waves per workgroup (one workgroup per CU); STAGES: depth of
-// the K and V rings.
-template <> struct FwdCfg<64> { static constexpr int BC = 64, WAVES = 8, STAGES = 3; };
-template <> struct FwdCfg<128> { static constexpr int BC = 64, WAVES = 8, STAGES = 3; };
-template <> struct FwdCfg<256> { static constexpr int BC = 64, WAVES = 4, STAGES = 2; };
+// the K ring (the V ring has one more stage under ping-pong).
+// PP: ping-pong schedule between the two waves of each SIMD (needs two waves per SIMD).
+template <> struct FwdCfg<64> { static constexpr int BC = 64, WAVES = 8, STAGES = 3; static constexpr bool PP = true; };
+template <> struct FwdCfg<128> { static constexpr int BC = 64, WAVES = 8, STAGES = 3; static constexpr bool PP = true; };
+template <> struct FwdCfg<256> { static constexpr int BC = 64, WAVES = 4, STAGES = 2; static constexpr bool PP = false; };
 
 constexpr int kQW = 32;                  // query rows per wave
 template <int D> constexpr int fwd_rows() { return FwdCfg<D>::WAVES * kQW; }   // per workgroup
@@ -135,11 +139,16 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::WAVES, 1) void fwd_kernel(FwdParams
   constexpr int KMIN = KPlan::NI / kWaves, VMIN = VPlan::NI / kWaves;
   static_assert(KMIN >= 1 && VMIN >= 1, "every wave takes part in each tile's DMA");
 
-  // K ring then V ring, NS stages each. Tile t lives in stage t % NS. Loop iteration j
-  // reads K(j+1) and V(j), and requests V(j+NS-1) and K(j+NS) into the stages that
-  // iteration j-1 finished reading.
+  // Ping-pong: the second wave of each SIMD runs the P~V half of every fast tile one
+  // barrier interval late, so that on each SIMD one wave exponentiates while the other
+  // multiplies.
+  constexpr bool PP = FwdCfg<D>::PP;
+  constexpr int VS = NS + (PP ? 1 : 0);
+  // K ring (NS stages) then V ring (VS stages); tile t lives in stage t % NS (t % VS).
+  // Loop iteration j reads K(j+1) and V(j) (and V(j-1) in the late waves), and requests
+  // V(j+NS-1) and K(j+NS) into stages no wave reads after the previous barrier.
   constexpr int KBYTES = KPlan::BYTES, VBYTES = VPlan::BYTES;
-  __shared__ __attribute__((aligned(1024))) char smem[NS * KBYTES + NS * VBYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[NS * KBYTES + VS * VBYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps loop control scalar
@@ -169,7 +178,7 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::WAVES, 1) void fwd_kernel(FwdParams
   // Stage offsets pass through readfirstlane: opaque to loop strength reduction, which would
   // otherwise keep one induction register per operand address.
   auto kst = [&](int j) { return smem + __builtin_amdgcn_readfirstlane((j % NS) * KBYTES); };
-  auto vst = [&](int j) { return smem + NS * KBYTES + __builtin_amdgcn_readfirstlane((j % NS) * VBYTES); };
+  auto vst = [&](int j) { return smem + NS * KBYTES + __builtin_amdgcn_readfirstlane((j % VS) * VBYTES); };
   const int k_lane = k_lane_off<D>(lane), v_lane = v_lane_off<D>(lane);
   auto is_edge = [&](int j) { const int k0 = j * BC; return (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0); };
   uint32_t kvoff[KPlan::NPW], vvoff[VPlan::NPW];
@@ -253,9 +262,8 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::WAVES, 1) void fwd_kernel(FwdParams
     }
   };
 
-  // Interior tiles (neither tile j nor j+1 masked; masking only ever starts near the end of
-  // a wave's key range): the pipelined form, with the instruction order written out.
-  // Block 1 issues one S(j+1) MFMA per step and, under it, exponentiates EPS scores of
+  // Interior tiles (neither tile j nor j+1 masked): the pipelined form, with the instruction
+  // order written out. Block 1 issues one S(j+1) MFMA per step and, under it, exponentiates EPS scores of
   // tile j (packing the first 16-key chunk of P~ as soon as it is complete). Block 2 issues
   // one P~(j)V(j) MFMA per step and, under it, packs the next chunk of P~ (one conversion
   // per step, ahead of the step that consumes it), adds the row-sum terms and folds tile
@@ -269,17 +277,17 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::WAVES, 1) void fwd_kernel(FwdParams
   constexpr int C0 = 8 / EPS;         // block-1 step that packs the first conversion of chunk 0
   static_assert(EPS * S1 == 16 * NKB && MPS * S2 == 16 * NKB && EPS >= 1 && (MPS == 1 || MPS % 2 == 0), "step split");
   static_assert(C0 + 4 <= S1 && NDB % 2 == 0 && NDB <= 8, "chunk 0 packs inside block 1");
-  auto fast_iter = [&](int jj, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) {
-    prefetch(jj);
-    rescale();
+  // P~ of the tile in flight: fp32 values, then 16-bit pairs (word 4q + u of 16-key chunk q
+  // holds keys 8q + 2u, 8q + 2u + 1). Scalars, not vectors: a vector filled one element at a
+  // time would keep its previous value alive around the loop.
+  float e[16 * NKB];
+  uint32_t pw[8 * NKB];
+  auto pack = [&](int q, int u) { pw[4 * q + u] = pack2<BF16>(e[8 * q + 2 * u], e[8 * q + 2 * u + 1]); };
+  // Block 1 of tile jj: S(jj+1) = K(jj+1) Q^T into nxt, P~(jj) = exp2(cur*c - m) into e.
+  auto blk1 = [&](int jj, const f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) __attribute__((always_inline)) {
     const float m_use = m_run;
     const char* kn = kst(jj + 1) + k_lane;
-    const char* vc = vst(jj) + v_lane;
-    u32x4 pk[2 * NKB];
     u32x4 kop[S1];
-    float e[16 * NKB];
-    // conversion u (0..3) of chunk q: two P~ values of keys 8q + 2u, 8q + 2u + 1
-    auto pack = [&](int q, int u) { pk[q][u] = pack2<BF16>(e[8 * q + 2 * u], e[8 * q + 2 * u + 1]); };
     __builtin_amdgcn_sched_barrier(0);
     // step t multiplies key block t % NKB at k-step t / NKB: consecutive MFMAs accumulate
     // into different registers.
@@ -294,12 +302,22 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::WAVES, 1) void fwd_kernel(FwdParams
       for (int u = 0; u < EPS; ++u) {
         const int i = EPS * t + u;
         e[i] = fast_exp2(fmaf(cur[i >> 4][i & 15], c, -m_use));
+        pin(e[i]);   // computed here: the compiler would sink it to its use in block 2
       }
-      if (t >= C0 && t < C0 + 4) pack(0, t - C0);
+      if (t >= C0 && t < C0 + 4) {
+        pack(0, t - C0);
+        pin(pw[t - C0]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  // Block 2 of tile jj: O^T += V(jj)^T P~(jj)^T, the row sum of P~(jj), and the row maximum
+  // of the scores nxt = S(jj+1) that block 1 of tile jj produced.
+  auto blk2 = [&](int jj, const f32x16 (&nxt)[NKB]) __attribute__((always_inline)) {
+    const char* vc = vst(jj) + v_lane;
     u32x4 vop[S2];
     float mx = -INFINITY, psum = 0.f;
+    __builtin_amdgcn_sched_barrier(0);
     // step t adds key chunk t / NDB into output block t % NDB (different accumulators in turn)
 #pragma unroll
     for (int t = 0; t < PF; ++t) vop[t] = lds_vt<D>(vc, t / NDB, t % NDB);
@@ -307,7 +325,7 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::WAVES, 1) void fwd_kernel(FwdParams
     for (int t = 0; t < S2; ++t) {
       if (t + PF < S2) vop[t + PF] = lds_vt<D>(vc, (t + PF) / NDB, (t + PF) % NDB);
       const int i = t % NDB, cidx = t / NDB;
-      oacc[i] = mfma32x16<BF16>(vop[t], pk[cidx], oacc[i]);
+      oacc[i] = mfma32x16<BF16>(vop[t], u32x4{pw[4 * cidx], pw[4 * cidx + 1], pw[4 * cidx + 2], pw[4 * cidx + 3]}, oacc[i]);
       // chunk cidx + 1 is consumed from step NDB * (cidx + 1): convert it during chunk cidx,
       // CPS conversions every SS-th step
       constexpr int CPS = NDB >= 4 ? 1 : 4 / NDB, SS = NDB >= 4 ? NDB / 4 : 1;
@@ -333,19 +351,40 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::WAVES, 1) void fwd_kernel(FwdParams
     l_run += psum;
     mx = xhalf_max(mx);
     mx_next = mx * c;
-    end_tile(jj);
+  };
+  // Tile jj runs the fast path when tiles jj and jj+1 need no mask: jj + 1 < nkt_w and
+  // !is_edge(jj + 1) (masking only ever starts near the end of a wave's key range, so the
+  // fast tiles are a prefix). The tests are written out in the loop: a helper lambda for
+  // them changes how the loops are optimised and costs registers in the causal kernels.
+  // One fast iteration. The late waves (ping-pong) take the barrier that ends iteration jj
+  // between the two blocks: their block 2 of tile jj then runs after that barrier, beside
+  // the early waves' block 1 of tile jj+1, so on each SIMD one wave's exponentials overlap
+  // the other wave's P~V MFMAs. The barrier count is unchanged; V(jj) is read one barrier
+  // interval later, which the extra V stage covers.
+  auto fast_iter = [&](auto late, int jj, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) __attribute__((always_inline)) {
+    prefetch(jj);
+    rescale();
+    blk1(jj, cur, nxt);
+    if constexpr (decltype(late)::value) end_tile(jj);
+    blk2(jj, nxt);
+    if constexpr (!decltype(late)::value) end_tile(jj);
   };
   int j = 0;
-  for (; j + 2 < nkt_w && !is_edge(j + 2); j += 2) {   // sc/sn swap roles: no copies
-    fast_iter(j, sc, sn);
-    fast_iter(j + 1, sn, sc);
-  }
-  if (j + 1 < nkt_w && !is_edge(j + 1)) {
-    fast_iter(j, sc, sn);
+  auto fast_loop = [&](auto late) __attribute__((always_inline)) {
+    for (; j + 2 < nkt_w && !is_edge(j + 2); j += 2) {   // sc/sn swap roles: no copies
+      fast_iter(late, j, sc, sn);
+      fast_iter(late, j + 1, sn, sc);
+    }
+    if (j + 1 < nkt_w && !is_edge(j + 1)) {
+      fast_iter(late, j, sc, sn);
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) sc[kb] = sn[kb];
-    ++j;
-  }
+      for (int kb = 0; kb < NKB; ++kb) sc[kb] = sn[kb];
+      ++j;
+    }
+  };
+  // Waves w and w + W/2 share a SIMD (waves are placed on the SIMDs round-robin).
+  if (PP && wave >= kWaves / 2) fast_loop(std::true_type{});
+  else fast_loop(std::false_type{});
   // Remaining tiles, in order: masked tiles and the tail of the key range (and, for waves
   // with nothing left to compute, only the ring bookkeeping every wave takes part in).
   for (; j < nkt; ++j) {
