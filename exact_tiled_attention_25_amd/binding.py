@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libattn.so")
 ATTN_BF16, ATTN_FP16 = 0, 1
 FP8_BLOCK = 64
 EXPORTS = ("attn_fwd", "attn_bwd_workspace_bytes", "attn_bwd", "attn_fp8_quantize",
-           "attn_fwd_fp8", "attn_strerror")
+           "attn_fp8_quantize_per_tensor", "attn_fwd_fp8", "attn_strerror")
 _DTYPE_CODE = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_FP16}
 
 _lib = None
@@ -48,8 +48,9 @@ def load(path=None):
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     L.attn_bwd.restype = i
-    L.attn_fp8_quantize.argtypes = [vp, vp, vp, i, i, i, i, i, i, u64, vp]
-    L.attn_fp8_quantize.restype = i
+    for fn in (L.attn_fp8_quantize, L.attn_fp8_quantize_per_tensor):
+        fn.argtypes = [vp, vp, vp, i, i, i, i, i, i, u64, vp]
+        fn.restype = i
     L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, vp, u64, i, vp]
     L.attn_fwd_fp8.restype = i
     L.attn_strerror.argtypes = [i]
@@ -136,8 +137,9 @@ def attn_bwd(q, k, v, o, lse, do, causal=False, scale=None, dq=None, dk=None, dv
     return dq, dk, dv
 
 
-def attn_fp8_quantize(x, rotate, hadamard_seed=0, x8=None, descale=None, stream=None):
-    """e4m3 codes [B, N, H, d] (uint8) and fp32 descales [B, H, ceil(N/64)] of x."""
+def attn_fp8_quantize(x, rotate, hadamard_seed=0, x8=None, descale=None, stream=None, per_tensor=False):
+    """e4m3 codes [B, N, H, d] (uint8) and fp32 descales [B, H, ceil(N/64)] of x: one descale
+    per 64-row block, or with per_tensor=True one descale for all of x (in every entry)."""
     _tensor(x, "x", dtypes=tuple(_DTYPE_CODE))
     B, N, H, d = x.shape
     nblk = (N + FP8_BLOCK - 1) // FP8_BLOCK
@@ -145,10 +147,16 @@ def attn_fp8_quantize(x, rotate, hadamard_seed=0, x8=None, descale=None, stream=
           else _tensor(x8, "x8", x.shape, (torch.uint8,), x.device))
     descale = (torch.empty((B, H, nblk), dtype=torch.float32, device=x.device) if descale is None
                else _tensor(descale, "descale", (B, H, nblk), (torch.float32,), x.device))
-    _check("attn_fp8_quantize", load().attn_fp8_quantize(_ptr(x), _ptr(x8), _ptr(descale), B, H, N, d,
-                                                         _DTYPE_CODE[x.dtype], int(bool(rotate)),
-                                                         int(hadamard_seed) & (2 ** 64 - 1), _stream(x, stream)))
+    name = "attn_fp8_quantize_per_tensor" if per_tensor else "attn_fp8_quantize"
+    _check(name, getattr(load(), name)(_ptr(x), _ptr(x8), _ptr(descale), B, H, N, d,
+                                       _DTYPE_CODE[x.dtype], int(bool(rotate)),
+                                       int(hadamard_seed) & (2 ** 64 - 1), _stream(x, stream)))
     return x8, descale
+
+
+def attn_fp8_quantize_per_tensor(x, rotate, hadamard_seed=0, x8=None, descale=None, stream=None):
+    """attn_fp8_quantize with one descale for the whole tensor."""
+    return attn_fp8_quantize(x, rotate, hadamard_seed, x8, descale, stream, per_tensor=True)
 
 
 def attn_fwd_fp8(q8, k8, v8, descale_q, descale_k, descale_v, causal=False, scale=None,

@@ -100,21 +100,35 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
   return launched(attn::launch_bwd(dtype == ATTN_BF16, d, causal != 0, p, (hipStream_t)stream));
 }
 
-attn_status_t attn_fp8_quantize(const void* x, uint8_t* x8, float* descale,
-                                int B, int H, int N, int d, attn_dtype_t dtype,
-                                int rotate, uint64_t hadamard_seed, attn_stream_t stream) {
+static attn_status_t fp8_quantize(const void* x, uint8_t* x8, float* descale, int B, int H, int N,
+                                  int d, attn_dtype_t dtype, int rotate, uint64_t hadamard_seed,
+                                  bool per_tensor, attn_stream_t stream) {
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_EINVAL;
   bool empty = false;
   attn_status_t st = check_sizes(B, H, N, d, &empty);
   if (st != ATTN_OK || empty) return st;
+  // one workgroup per 64-row block (and, per tensor, one int count of all blocks)
+  if ((double)B * H * ((N + 63) / 64) >= 2147483647.0) return ATTN_EUNSUPPORTED;
   if (!x || !x8 || !descale) return ATTN_EINVAL;
   if ((st = check_device()) != ATTN_OK) return st;
-  attn::Fp8QuantParams p{x, x8, descale, B, H, N, rotate != 0, {0, 0, 0, 0, 0, 0, 0, 0}};
+  attn::Fp8QuantParams p{x, x8, descale, B, H, N, rotate != 0, {0, 0, 0, 0, 0, 0, 0, 0}, per_tensor ? 1 : 0};
   if (rotate)
     for (int t = 0; t < d; ++t)
       if (splitmix64_output(hadamard_seed, (uint64_t)t) >> 63) p.neg[t >> 5] |= 1u << (t & 31);
   (void)hipGetLastError();
   return launched(attn::launch_fp8_quantize(dtype == ATTN_BF16, d, p, (hipStream_t)stream));
+}
+
+attn_status_t attn_fp8_quantize(const void* x, uint8_t* x8, float* descale,
+                                int B, int H, int N, int d, attn_dtype_t dtype,
+                                int rotate, uint64_t hadamard_seed, attn_stream_t stream) {
+  return fp8_quantize(x, x8, descale, B, H, N, d, dtype, rotate, hadamard_seed, false, stream);
+}
+
+attn_status_t attn_fp8_quantize_per_tensor(const void* x, uint8_t* x8, float* descale,
+                                           int B, int H, int N, int d, attn_dtype_t dtype,
+                                           int rotate, uint64_t hadamard_seed, attn_stream_t stream) {
+  return fp8_quantize(x, x8, descale, B, H, N, d, dtype, rotate, hadamard_seed, true, stream);
 }
 
 attn_status_t attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,

@@ -12,7 +12,10 @@
 //   d/4 contiguous elements each. Signs, then the Hadamard butterfly (log2(d/4) in-thread
 //   stages and 2 stages across the row's 4 lanes), times 1/sqrt(d); block amax by wave and
 //   LDS reduction; descale = amax/448 (1 for an all-zero block); code = RNE(y / descale)
-//   after clamping to +-448 (the hardware convert is not saturating).
+//   after clamping to +-448 (the hardware convert is not saturating). Per-tensor mode (the
+//   single-scale baseline that block quantisation is compared with): the same kernel
+//   writes each block's amax, one workgroup reduces them to the tensor's descale and
+//   writes it to every block's slot, and the kernel runs again to encode with it.
 //
 // fwd_fp8_kernel: the bf16 forward's structure with v_mfma_f32_32x32x64_f8f6f4 (e4m3 x
 //   e4m3, fp32 accumulate) on 64-key tiles (one K and one V scale block each): DMA ring,
@@ -48,7 +51,11 @@ __device__ __forceinline__ uint32_t cvt4_fp8(float a, float b, float c, float d)
 __device__ __forceinline__ float clamp448(float x) { return fminf(fmaxf(x, -kE4m3Max), kE4m3Max); }
 
 // ---------------------------------------------------------------- quantiser
-template <bool BF16, int D>
+// MODE kQuantBlock: the block's own descale, codes and descale written. kQuantAmax: only
+// the block's amax (of the rotated values) is written, to the descale slot. kQuantFixed:
+// codes with the descale already in the slot (which is left as it is).
+constexpr int kQuantBlock = 0, kQuantAmax = 1, kQuantFixed = 2;
+template <bool BF16, int D, int MODE>
 __global__ __launch_bounds__(256) void fp8_quant_kernel(Fp8QuantParams p) {
   constexpr int EPT = D / 4;   // elements per thread (4 threads per row)
   const int tid = threadIdx.x, t = tid & 3, rloc = tid >> 2;
@@ -99,16 +106,26 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(Fp8QuantParams p) {
 #pragma unroll
     for (int e = 0; e < EPT; ++e) y[e] *= inv_sqrt_d;
   }
-  float amax = 0.f;
+  float* const ds_slot = p.descale + ((size_t)b * H + h) * nblk + blk;
+  float descale;
+  if constexpr (MODE == kQuantFixed) {
+    descale = *ds_slot;
+  } else {
+    float amax = 0.f;
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) amax = fmaxf(amax, fabsf(y[e]));
+    for (int e = 0; e < EPT; ++e) amax = fmaxf(amax, fabsf(y[e]));
 #pragma unroll
-  for (int m = 32; m > 0; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-  __shared__ float red[4];
-  if ((tid & 63) == 0) red[tid >> 6] = amax;
-  __syncthreads();
-  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float descale = amax > 0.f ? amax / kE4m3Max : 1.0f;
+    for (int m = 32; m > 0; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+    __shared__ float red[4];
+    if ((tid & 63) == 0) red[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if constexpr (MODE == kQuantAmax) {
+      if (tid == 0) *ds_slot = amax;
+      return;
+    }
+    descale = amax > 0.f ? amax / kE4m3Max : 1.0f;
+  }
 
   uint32_t codes[EPT / 4];
 #pragma unroll
@@ -119,7 +136,26 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(Fp8QuantParams p) {
   for (int c = 0; c < EPT / 16; ++c)
     buf_store16(r8, (uint32_t)row * H * D + t * EPT + 16 * c,
                 u32x4{codes[4 * c], codes[4 * c + 1], codes[4 * c + 2], codes[4 * c + 3]});
-  if (tid == 0) p.descale[((size_t)b * H + h) * nblk + blk] = descale;
+  if (MODE == kQuantBlock && tid == 0) *ds_slot = descale;
+}
+
+// One workgroup: the tensor's descale from the n block amaxes in d (written by kQuantAmax),
+// written back to all n slots: fp32(amax / 448), or 1 if the whole tensor is zero. Every
+// thread has read its slots before the barrier that precedes the first write.
+__global__ __launch_bounds__(1024) void fp8_tensor_scale_kernel(float* d, int n) {
+  const int tid = threadIdx.x;
+  float amax = 0.f;
+  for (int i = tid; i < n; i += 1024) amax = fmaxf(amax, d[i]);
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+  __shared__ float red[16];
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = red[0];
+#pragma unroll
+  for (int w = 1; w < 16; ++w) amax = fmaxf(amax, red[w]);
+  const float descale = amax > 0.f ? amax / kE4m3Max : 1.0f;
+  for (int i = tid; i < n; i += 1024) d[i] = descale;
 }
 
 // ---------------------------------------------------------------- fp8 attention
@@ -503,7 +539,17 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
 template <bool BF16, int D>
 hipError_t launch_q(const Fp8QuantParams& p, hipStream_t s) {
   const int nblk = (p.N + 63) / 64;
-  hipLaunchKernelGGL((fp8_quant_kernel<BF16, D>), dim3((unsigned)(p.B * p.H * nblk)), dim3(256), 0, s, p);
+  const dim3 grid((unsigned)(p.B * p.H * nblk));
+  if (!p.per_tensor) {
+    hipLaunchKernelGGL((fp8_quant_kernel<BF16, D, kQuantBlock>), grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((fp8_quant_kernel<BF16, D, kQuantAmax>), grid, dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fp8_tensor_scale_kernel, dim3(1), dim3(1024), 0, s, p.descale, p.B * p.H * nblk);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((fp8_quant_kernel<BF16, D, kQuantFixed>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

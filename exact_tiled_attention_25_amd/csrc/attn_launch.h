@@ -38,6 +38,7 @@ struct Fp8QuantParams {
   int B, H, N;
   int rotate;
   uint32_t neg[8];  // bit t set: dim t of the random sign vector is -1 (d <= 256)
+  int per_tensor;   // one descale for the whole tensor instead of one per 64-row block
 };
 
 struct Fp8FwdParams {

@@ -79,6 +79,20 @@ attn_status_t attn_fp8_quantize(const void* x, uint8_t* x8, float* descale,
                                 int B, int H, int N, int d, attn_dtype_t dtype,
                                 int rotate, uint64_t hadamard_seed, attn_stream_t stream);
 
+/* FP8 quantisation with ONE scale for the whole tensor: the per-tensor baseline that
+ * block quantisation is measured against (explainer, "FP8 accuracy controls"; the
+ * enterprise post "FlashAttention 3 Hardware Acceleration", sections "FP8 Accumulation"
+ * and "FP8 Validation": block scales replace a single scale for the entire tensor).
+ * Same arguments, rotation and encoding as attn_fp8_quantize; descale = fp32(amax/448)
+ * with amax over every (rotated) element of x (1 for an all-zero tensor), and that value is
+ * written to all B*H*ceil(N/64) descale entries, so attn_fwd_fp8 takes the result as is.
+ * B*H*ceil(N/64) must stay below 2^31. Runs three kernels on `stream`; the descale array
+ * holds intermediate values between them. */
+attn_status_t attn_fp8_quantize_per_tensor(const void* x, uint8_t* x8, float* descale,
+                                           int B, int H, int N, int d, attn_dtype_t dtype,
+                                           int rotate, uint64_t hadamard_seed,
+                                           attn_stream_t stream);
+
 /* FP8 forward attention ("FP8 layout conformance", "FP8 accuracy controls"):
  * O = softmax(scale * Qh Kh^T [+ mask]) Vh with Xh = e4m3(X8) * descale_X per 64-row block.
  * Q8 and K8 must have been rotated with the same seed (or both not at all); because the

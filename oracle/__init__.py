@@ -19,5 +19,6 @@ pinned by a ``-m "not gpu"`` test in ``tests/test_oracle_*.py``.
 from .attention import (forward, forward_rows, backward, head_forward, head_backward,  # noqa: F401
                         head_probs, flops_forward)
 from .fp8 import (e4m3_decode, e4m3_encode, e4m3_finite_values, splitmix64, hadamard_signs,  # noqa: F401
-                  sylvester_hadamard, rotation_matrix, quantize_blocks, dequantize_blocks,
+                  sylvester_hadamard, rotation_matrix, quantize_blocks, quantize_per_tensor,
+                  dequantize_blocks,
                   fp8_emulated_forward, FP8_BLOCK_ROWS, E4M3_MAX)

@@ -1,4 +1,5 @@
-"""FP8 (e4m3) forward attention oracle: codec, rotation, block quantiser, emulated forward.
+"""FP8 (e4m3) forward attention oracle: codec, rotation, block and per-tensor quantisers,
+emulated forward.
 
 What is computed (page "FlashAttention-3: Hopper Asynchrony and FP8 Attention", Deep Dive
 "FP8 accuracy controls"):
@@ -28,7 +29,10 @@ Pins (tests/test_oracle_fp8.py): OCP e4m3 facts (max 448, min normal 2^-6, min s
 2^-9, 1.0 = 0x38), exhaustive encode/decode round trip over all 256 codes with RNE at every
 midpoint and saturation; scipy.linalg.hadamard; M M^T = I; (QM)(KM)^T = QK^T; SplitMix64
 against the published reference outputs for seed 0; per-element error bound of the block
-quantiser and exact mapping of each block's amax to the +-448 code.
+quantiser and exact mapping of each block's amax to the +-448 code; the per-tensor
+quantiser: same error bound, only the tensor's amax reaches +-448, its descale is the
+largest block descale, power-of-two scaling of the input moves only the descale, and on a
+single 64-row block it equals the block quantiser.
 """
 import numpy as np
 
@@ -132,6 +136,27 @@ def quantize_blocks(x, rotate, seed=0, block=FP8_BLOCK_ROWS):
                 descale[b, h, j] = ds
                 scaled = tile.astype(np.float32) / ds          # fp32 / fp32, correctly rounded
                 codes[b, j * block:(j + 1) * block, h] = e4m3_encode(scaled.astype(np.float64))
+    return codes, descale, y
+
+
+def quantize_per_tensor(x, rotate, seed=0, block=FP8_BLOCK_ROWS):
+    """Quantise x [B, N, H, d] to e4m3 codes with ONE fp32 descale for the whole tensor.
+
+    The per-tensor baseline that block quantisation is compared with (explainer, "FP8
+    accuracy controls"; enterprise post, "FP8 Accumulation" and "FP8 Validation": block
+    scales instead of a single scale for the entire tensor). amax runs over every element
+    of the (rotated) tensor, all batches and heads; descale and codes follow the same fp32
+    arithmetic as quantize_blocks. The descale is returned in the block layout
+    [B, H, ceil(N/64)] with every entry equal, so dequantize_blocks and
+    fp8_emulated_forward take it unchanged. Returns (codes, descale, y) like quantize_blocks.
+    """
+    x = _f64(x)
+    B, N, H, d = x.shape
+    y = x @ rotation_matrix(d, seed) if rotate else x.copy()
+    amax = np.float32(np.abs(y).max()) if y.size else np.float32(0.0)
+    ds = np.float32(amax / np.float32(E4M3_MAX)) if amax > 0 else np.float32(1.0)
+    codes = e4m3_encode((y.astype(np.float32) / ds).astype(np.float64))
+    descale = np.full((B, H, (N + block - 1) // block), ds, dtype=np.float32)
     return codes, descale, y
 
 

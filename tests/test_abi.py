@@ -59,5 +59,7 @@ def test_null_pointers_rejected(lib):
     assert lib.attn_bwd(None, None, None, None, None, None, None, None, None, 1, 1, 16, 64, 0, 0.125, 0,
                         None, 0, None) == 1
     assert lib.attn_fp8_quantize(None, None, None, 1, 1, 16, 64, 0, 1, 0, None) == 1
+    assert lib.attn_fp8_quantize_per_tensor(None, None, None, 1, 1, 16, 64, 0, 1, 0, None) == 1
+    assert lib.attn_fp8_quantize_per_tensor(None, None, None, 1, 1, 16, 100, 0, 1, 0, None) == 2
     assert lib.attn_fwd_fp8(None, None, None, None, None, 1, 1, 16, 64, 0, 0.125, None, None, None, 0, 0,
                             None) == 1

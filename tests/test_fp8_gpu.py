@@ -9,6 +9,8 @@
   relative RMSE of 0.06, the budget of rounding P~ to e4m3 (about 2^-4/sqrt(3) = 3.6% rms).
 * End to end (GPU quantiser + GPU attention) vs the fp64 oracle on the original bf16 inputs:
   RMSE(O) <= 3e-2 on the 0.1%-outlier workload, with and without the Hadamard rotation.
+* attn_fp8_quantize_per_tensor vs oracle.quantize_per_tensor (same code criteria), and the
+  four scaling modes (per tensor / per block, with / without rotation) compared end to end.
 """
 import numpy as np
 import pytest
@@ -26,8 +28,8 @@ def _binding():
     return binding
 
 
-def _compare_codes(codes_gpu, ds_gpu, x, rotate, seed):
-    codes_ref, ds_ref, y = oracle.quantize_blocks(x, rotate, seed)
+def _compare_codes(codes_gpu, ds_gpu, x, rotate, seed, quantize=None):
+    codes_ref, ds_ref, y = (quantize or oracle.quantize_blocks)(x, rotate, seed)
     if not rotate:
         np.testing.assert_array_equal(ds_gpu, ds_ref)
         np.testing.assert_array_equal(codes_gpu, codes_ref)
@@ -68,6 +70,32 @@ def test_quantizer_matches_oracle(lib, shape, dtype, rotate):
     torch.cuda.synchronize()
     nbad = _compare_codes(c8.cpu().numpy(), ds.cpu().numpy(), x, rotate, seed)
     log(f"  midpoint flips: {nbad}")
+
+
+@pytest.mark.parametrize("shape", [(1, 200, 3, 64), (2, 129, 2, 128), (1, 77, 2, 256), (3, 1, 1, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("rotate", [False, True], ids=["plain", "hadamard"])
+def test_quantizer_per_tensor_matches_oracle(lib, shape, rotate):
+    B, N, H, d = shape
+    log(f"quant per-tensor B={B} N={N} H={H} d={d} rotate={rotate}")
+    x = workloads.make_inputs(B, N, H, d, "bf16", 43, outlier_frac=1e-2, outlier_sigma=10.0)["q"]
+    if N >= 128:
+        x[:, 64:128, 0] = 0                       # an all-zero block: zero codes, shared descale
+    seed = 0xBEEF + d
+    b = _binding()
+    c8, ds = b.attn_fp8_quantize_per_tensor(x.cuda(), rotate, seed)
+    torch.cuda.synchronize()
+    ds = ds.cpu().numpy()
+    assert np.all(ds == ds.flat[0])
+    nbad = _compare_codes(c8.cpu().numpy(), ds, x, rotate, seed, oracle.quantize_per_tensor)
+    log(f"  midpoint flips: {nbad}")
+
+
+def test_quantizer_per_tensor_all_zero(lib):
+    x = torch.zeros(2, 130, 2, 128, dtype=torch.bfloat16)
+    c8, ds = _binding().attn_fp8_quantize_per_tensor(x.cuda(), True, 7)
+    torch.cuda.synchronize()
+    assert torch.all(ds.cpu() == 1.0) and torch.all(c8.cpu() & 0x7F == 0)
 
 
 def test_quantizer_signs_follow_seed(lib):
@@ -111,12 +139,12 @@ def test_fwd_fp8_matches_emulation(lib, shape, causal, out):
     assert eo["max_rel"] <= 0.25, eo
 
 
-def _end_to_end(x, causal, rotate, seed):
+def _end_to_end(x, causal, rotate, seed, per_tensor=False):
     b = _binding()
     q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
-    q8, dq = b.attn_fp8_quantize(q, rotate, seed)
-    k8, dk = b.attn_fp8_quantize(k, rotate, seed)
-    v8, dv = b.attn_fp8_quantize(v, False, seed)
+    q8, dq = b.attn_fp8_quantize(q, rotate, seed, per_tensor=per_tensor)
+    k8, dk = b.attn_fp8_quantize(k, rotate, seed, per_tensor=per_tensor)
+    v8, dv = b.attn_fp8_quantize(v, False, seed, per_tensor=per_tensor)
     o, lse = b.attn_fwd_fp8(q8, k8, v8, dq, dk, dv, causal, hadamard_seed=seed)
     torch.cuda.synchronize()
     return to64(o), to64(lse)
@@ -166,3 +194,31 @@ def test_fp8_hadamard_gain_across_seeds(lib):
         log(f"  plain={rm[False]:.4e} hadamard={rm[True]:.4e} ratio={ratios[-1]:.4f}")
     log(f"  ratio mean={np.mean(ratios):.4f} min={np.min(ratios):.4f} max={np.max(ratios):.4f}")
     assert max(ratios) < 1.0
+
+
+def test_fp8_scaling_modes_compared(lib):
+    """The accuracy comparison of the pages' FP8 controls on the outlier workload: one scale
+    per tensor vs one per 64-row block, each with and without the Hadamard rotation, as RMSE
+    of O against the fp64 oracle on the original inputs (sampled rows of several heads)."""
+    cfg = workloads.CONFIGS["c5"]
+    B, N, H, d = cfg["B"], cfg["N"], cfg["H"], cfg["d"]
+    log(f"fp8 scaling modes c5 B={B} N={N} H={H} d={d}")
+    x = workloads.config_inputs("c5", with_do=False)
+    rng = np.random.default_rng(7)
+    heads = [(int(rng.integers(B)), int(rng.integers(H))) for _ in range(4)]
+    rows = rng.choice(N, 160, replace=False)
+    ref = np.concatenate([oracle.forward_rows(x["q"], x["k"], x["v"], b_, h_, rows, False)[0] for b_, h_ in heads])
+    rm = {}
+    for per_tensor in (True, False):
+        for rotate in (False, True):
+            o, _ = _end_to_end(x, False, rotate, seed=0x5EED, per_tensor=per_tensor)
+            e = errs(np.concatenate([o[b_, rows, h_] for b_, h_ in heads]), ref)
+            rm[(per_tensor, rotate)] = e["rmse"]
+            log(f"  {'per-tensor' if per_tensor else 'per-block '} rotate={rotate}: RMSE={e['rmse']:.4e} "
+                f"relRMSE={e['rel_rmse']:.4e}")
+    log(f"  per-tensor / block+Hadamard = {rm[(True, False)] / rm[(False, True)]:.4f}")
+    assert rm[(False, True)] <= 3e-2 and rm[(False, False)] <= 3e-2
+    # the direction the pages report: both controls beat the per-tensor baseline, and the
+    # rotation helps under a single scale (the block-vs-rotation ordering is only reported)
+    assert rm[(False, True)] < rm[(True, False)]
+    assert rm[(True, True)] < rm[(True, False)]

@@ -124,6 +124,58 @@ def test_block_quantizer_bounds(rotate):
     _check_block_bounds(x, codes, descale, y)
 
 
+@pytest.mark.parametrize("rotate", [False, True])
+def test_per_tensor_quantizer(rotate):
+    """One scale for the whole tensor: every element within half an e4m3 step of its value
+    at that scale; only the tensor's largest element(s) reach the +-448 code; the descale
+    is the largest of the block descales; power-of-two input scaling moves only the
+    descale."""
+    x = RNG.standard_normal((2, 150, 3, 64))
+    x[1, 100, 2, 7] = -55.0                   # the tensor's outlier, in one block of one head
+    x[0, 64:128, 1] = 0.0                     # an all-zero block keeps its codes at zero
+    codes, descale, y = oracle.quantize_per_tensor(x, rotate, seed=5)
+    assert descale.shape == (2, 3, 3) and descale.dtype == np.float32
+    assert np.all(descale == descale.flat[0])
+    ds = float(descale.flat[0])
+    amax = np.abs(y).max()
+    assert abs(ds * 448.0 - amax) <= amax * 2.0 ** -22
+    deq = oracle.e4m3_decode(codes) * ds
+    bound = np.maximum(np.abs(y) * 2.0 ** -4, ds * 2.0 ** -10) * (1 + 1e-9)
+    assert np.all(np.abs(deq - y) <= bound)
+    top = np.abs(y) == amax
+    assert np.all(codes[top] & 0x7F == 0x7E)
+    assert np.all(codes[~top] & 0x7F < 0x7E) or np.abs(y[~top]).max() * 448.0 / amax > 416.0
+    assert np.all(codes[0, 64:128, 1] & 0x7F == 0)
+    # the single descale is the largest descale of the blocks that are not all zero (an
+    # all-zero block's own descale is 1 by definition)
+    _, bds, _ = oracle.quantize_blocks(x, rotate, seed=5)
+    nonzero = np.abs(y).reshape(2, 150, 3, 64).max(axis=3)
+    nz = np.array([[[nonzero[b_, j * 64:(j + 1) * 64, h_].max() > 0 for j in range(3)] for h_ in range(3)]
+                   for b_ in range(2)])
+    assert ds == bds[nz].max() and not nz.all()
+    # scaling the input by 2^-3 scales the descale by 2^-3 and keeps every code
+    c2, d2, _ = oracle.quantize_per_tensor(x * 0.125, rotate, seed=5)
+    np.testing.assert_array_equal(c2, codes)
+    assert float(d2.flat[0]) == ds * 0.125
+
+
+def test_per_tensor_equals_block_on_one_block():
+    x = RNG.standard_normal((1, 50, 1, 128))
+    for rotate in (False, True):
+        c1, d1, _ = oracle.quantize_per_tensor(x, rotate, seed=9)
+        c2, d2, _ = oracle.quantize_blocks(x, rotate, seed=9)
+        np.testing.assert_array_equal(c1, c2)
+        np.testing.assert_array_equal(d1, d2)
+    # with several blocks they differ: small blocks keep finer codes under their own scale
+    x = RNG.standard_normal((1, 128, 1, 64))
+    x[0, 0, 0, 0] = 300.0
+    c1, d1, y = oracle.quantize_per_tensor(x, False)
+    c2, d2, _ = oracle.quantize_blocks(x, False)
+    e1 = np.abs(oracle.dequantize_blocks(c1, d1) - y)[0, 64:].max()
+    e2 = np.abs(oracle.dequantize_blocks(c2, d2) - y)[0, 64:].max()
+    assert d1[0, 0, 1] > d2[0, 0, 1] and e1 > e2
+
+
 def test_rotated_quantised_scores_track_exact_scores():
     x_q = RNG.standard_normal((1, 128, 1, 128))
     x_k = RNG.standard_normal((1, 128, 1, 128))

@@ -117,10 +117,35 @@ def _rotation_unnormalised(d, seed):
     return F.hadamard_signs(seed, d)[:, None] * F.sylvester_hadamard(d)
 
 
+def _per_tensor_scale_per_head(x, rotate, seed=0, block=F.FP8_BLOCK_ROWS):
+    """One scale per (batch, head) slice instead of one for the whole tensor."""
+    x = F._f64(x)
+    codes = np.empty(x.shape, dtype=np.uint8)
+    B, N, H, d = x.shape
+    descale = np.empty((B, H, (N + block - 1) // block), dtype=np.float32)
+    y = np.empty_like(x)
+    for b in range(B):
+        for h in range(H):
+            c, ds, yy = _ORIG_PER_TENSOR(x[b:b + 1, :, h:h + 1], rotate, seed, block)
+            codes[b, :, h], descale[b, h], y[b, :, h] = c[0, :, 0], ds[0, 0], yy[0, :, 0]
+    return codes, descale, y
+
+
+def _per_tensor_amax_before_rotation(x, rotate, seed=0, block=F.FP8_BLOCK_ROWS):
+    """The scale taken from the input before the rotation."""
+    codes, descale, y = _ORIG_PER_TENSOR(x, rotate, seed, block)
+    ds = np.float32(np.float32(np.abs(F._f64(x)).max()) / np.float32(F.E4M3_MAX))
+    return F.e4m3_encode((y.astype(np.float32) / ds).astype(np.float64)), np.full_like(descale, ds), y
+
+
+_ORIG_PER_TENSOR = F.quantize_per_tensor
+
 FP8_CASES = {
     "e4m3 bias 8": ("e4m3_decode", _decode_wrong_bias),
     "round half up": ("e4m3_encode", _encode_half_up),
     "Hadamard without 1/sqrt(d)": ("rotation_matrix", _rotation_unnormalised),
+    "per-tensor scale per head": ("quantize_per_tensor", _per_tensor_scale_per_head),
+    "per-tensor amax before rotation": ("quantize_per_tensor", _per_tensor_amax_before_rotation),
 }
 
 
@@ -129,6 +154,8 @@ def _fp8_pins():
         (TF.test_e4m3_ocp_fixed_points,),
         (TF.test_e4m3_midpoints_round_to_even_and_neighbours_to_nearest,),
         (TF.test_rotation_is_orthogonal_and_preserves_scores, 128),
+        (TF.test_per_tensor_quantizer, False),
+        (TF.test_per_tensor_quantizer, True),
     ]
 
 
