@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libattn.so")
 
 ATTN_BF16, ATTN_FP16 = 0, 1
 FP8_BLOCK = 64
-EXPORTS = ("attn_fwd", "attn_bwd_workspace_bytes", "attn_bwd", "attn_fp8_quantize",
+EXPORTS = ("attn_fwd", "attn_fwd_splitkv_workspace_bytes", "attn_fwd_splitkv",
+           "attn_bwd_workspace_bytes", "attn_bwd", "attn_fp8_quantize",
            "attn_fp8_quantize_per_tensor", "attn_fwd_fp8", "attn_strerror")
 _DTYPE_CODE = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_FP16}
 
@@ -44,6 +45,10 @@ def load(path=None):
     vp, i, f, sz, u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_uint64
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     L.attn_fwd.restype = i
+    L.attn_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.attn_fwd_splitkv_workspace_bytes.restype = sz
+    L.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    L.attn_fwd_splitkv.restype = i
     L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i]
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
@@ -108,6 +113,32 @@ def attn_fwd(q, k, v, causal=False, scale=None, o=None, lse=None, stream=None):
     _check("attn_fwd", load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                                        int(bool(causal)), _default_scale(d, scale), _DTYPE_CODE[q.dtype],
                                        _stream(q, stream)))
+    return o, lse
+
+
+def attn_fwd_splitkv_workspace_bytes(B, H, N, d, num_splits):
+    return int(load().attn_fwd_splitkv_workspace_bytes(B, H, N, d, num_splits))
+
+
+def attn_fwd_splitkv(q, k, v, num_splits, causal=False, scale=None, o=None, lse=None, workspace=None,
+                     stream=None):
+    """attn_fwd with each query tile's key range cut into num_splits parts (1..16), merged by
+    log-sum-exp; the workspace is allocated here when not given."""
+    _tensor(q, "q", dtypes=tuple(_DTYPE_CODE))
+    B, N, H, d = q.shape
+    _tensor(k, "k", q.shape, (q.dtype,), q.device)
+    _tensor(v, "v", q.shape, (q.dtype,), q.device)
+    o = torch.empty_like(q) if o is None else _tensor(o, "o", q.shape, (q.dtype,), q.device)
+    lse = (torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None
+           else _tensor(lse, "lse", (B, H, N), (torch.float32,), q.device))
+    if workspace is None:
+        need = attn_fwd_splitkv_workspace_bytes(B, H, N, d, num_splits)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _tensor(workspace, "workspace", device=q.device)
+    _check("attn_fwd_splitkv", load().attn_fwd_splitkv(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)), _default_scale(d, scale),
+        _DTYPE_CODE[q.dtype], int(num_splits), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(q, stream)))
     return o, lse
 
 

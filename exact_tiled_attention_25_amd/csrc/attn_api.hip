@@ -75,6 +75,35 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, flo
   return launched(attn::launch_fwd(dtype == ATTN_BF16, d, causal != 0, p, (hipStream_t)stream));
 }
 
+size_t attn_fwd_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits) {
+  if (B <= 0 || H <= 0 || N <= 0 || !supported_d(d) || num_splits < 1 || num_splits > 16) return 0;
+  return (size_t)num_splits * B * H * N * (size_t)(d + 1) * sizeof(float);
+}
+
+attn_status_t attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int H, int N, int d, int causal, float scale,
+                               attn_dtype_t dtype, int num_splits, void* workspace,
+                               size_t workspace_bytes, attn_stream_t stream) {
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_EINVAL;
+  if (bad_scale(scale)) return ATTN_EINVAL;
+  if (num_splits < 1 || num_splits > 16) return ATTN_EINVAL;
+  bool empty = false;
+  attn_status_t st = check_sizes(B, H, N, d, &empty);
+  if (st != ATTN_OK || empty) return st;
+  // grids: one workgroup per (query tile, head, batch, part); merge: 8 or more rows each
+  if ((double)B * H * ((N + 127) / 128) * num_splits >= 2147483647.0 || (double)B * H * N / 8 >= 2147483647.0)
+    return ATTN_EUNSUPPORTED;
+  if (!q || !k || !v || !o || !lse) return ATTN_EINVAL;
+  if (!workspace || workspace_bytes < attn_fwd_splitkv_workspace_bytes(B, H, N, d, num_splits))
+    return ATTN_EWORKSPACE;
+  if ((st = check_device()) != ATTN_OK) return st;
+  float* ws = (float*)workspace;
+  attn::FwdParams p{q, k, v, o, lse, B, H, N, (float)(scale * kLog2e), num_splits, ws,
+                    ws + (size_t)num_splits * B * H * N * d};
+  (void)hipGetLastError();
+  return launched(attn::launch_fwd_splitkv(dtype == ATTN_BF16, d, causal != 0, p, (hipStream_t)stream));
+}
+
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d) {
   (void)d;
   if (B <= 0 || H <= 0 || N <= 0) return 0;
@@ -155,7 +184,7 @@ const char* attn_strerror(attn_status_t s) {
     case ATTN_OK: return "success";
     case ATTN_EINVAL: return "invalid argument (null pointer, negative size, bad scale or enum)";
     case ATTN_EUNSUPPORTED: return "unsupported shape (head dim must be 64, 128 or 256; batch slice below 2 GiB)";
-    case ATTN_EWORKSPACE: return "workspace missing or too small (see attn_bwd_workspace_bytes)";
+    case ATTN_EWORKSPACE: return "workspace missing or too small (see attn_*_workspace_bytes)";
     case ATTN_ELAUNCH: return "kernel launch failed";
     case ATTN_EDEVICE: return "current device is not an MI355X-class gfx950 GPU";
   }

@@ -124,7 +124,11 @@ __device__ __forceinline__ void tile_pv(f32x16 (&oacc)[D / 32], const char* vl, 
     for (int cidx = 0; cidx < 2 * NKB; ++cidx) oacc[i] = mfma32x16<BF16>(lds_vt<D>(vl, cidx, i), pk[cidx], oacc[i]);
 }
 
-template <bool BF16, int D, bool CAUSAL>
+// SPLIT: the workgroup covers part `split` (tiles split*T .. split*T + T - 1, T =
+// p.split_tiles) of its query tile's key tiles; slots past the tile's last part exit at
+// once. With two or more parts it writes the part's O/l and L (natural log) to p.o_part,
+// p.lse_part (rows with no key in the part: L = -inf); a tile with one part writes O, L.
+template <bool BF16, int D, bool CAUSAL, bool SPLIT = false>
 __global__ __launch_bounds__(64 * FwdCfg<D>::WAVES, 1) void fwd_kernel(FwdParams p) {
   constexpr int BC = FwdCfg<D>::BC;
   constexpr int NKB = BC / 32;
@@ -157,8 +161,10 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::WAVES, 1) void fwd_kernel(FwdParams
   const int nqt = (N + kBR - 1) / kBR;
 
   const int work = xcd_remap(blockIdx.x, gridDim.x);
-  const int qi = work % nqt;
-  const int bh = work / nqt;
+  const int split = SPLIT ? work % p.splits : 0;   // parts of one query tile are neighbours
+  const int qwork = SPLIT ? work / p.splits : work;
+  const int qi = qwork % nqt;
+  const int bh = qwork / nqt;
   const int h = bh % H, b = bh / H;
   const int qt = CAUSAL ? nqt - 1 - qi : qi;
   const int q0 = qt * kBR + wave * kQW;
@@ -172,22 +178,33 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::WAVES, 1) void fwd_kernel(FwdParams
   const auto ro = make_rsrc((const char*)p.o + head_off, nrec);
 
   const int kend = CAUSAL ? min(N, (qt + 1) * kBR) : N;
-  const int nkt = (kend + BC - 1) / BC;
-  // tiles this wave computes: causal rows stop at the diagonal tile; rows past N compute none
-  const int nkt_w = q0 >= N ? 0 : CAUSAL ? min(nkt, (q0 + kQW - 1) / BC + 1) : nkt;
+  const int nkt_all = (kend + BC - 1) / BC;
+  // key tiles t0 .. t0 + nkt - 1 (global indices) of this workgroup: all, or one part
+  int t0 = 0, nkt = nkt_all, parts = 1;
+  if constexpr (SPLIT) {
+    parts = (nkt_all + p.split_tiles - 1) / p.split_tiles;
+    if (split >= parts) return;   // an unused slot (uniform over the workgroup, before any barrier)
+    t0 = split * p.split_tiles;
+    nkt = min(nkt_all, t0 + p.split_tiles) - t0;
+  }
+  // tiles this wave computes: causal rows stop at the diagonal tile; rows past N compute
+  // none. Every tile a wave computes holds an unmasked key of each of its rows (a tile
+  // starts at or before the wave's first row), so no computed row is fully masked.
+  const int nkt_w_all = q0 >= N ? 0 : CAUSAL ? min(nkt_all, (q0 + kQW - 1) / BC + 1) : nkt_all;
+  const int nkt_w = max(0, min(nkt, nkt_w_all - t0));
   // Stage offsets pass through readfirstlane: opaque to loop strength reduction, which would
   // otherwise keep one induction register per operand address.
   auto kst = [&](int j) { return smem + __builtin_amdgcn_readfirstlane((j % NS) * KBYTES); };
   auto vst = [&](int j) { return smem + NS * KBYTES + __builtin_amdgcn_readfirstlane((j % VS) * VBYTES); };
   const int k_lane = k_lane_off<D>(lane), v_lane = v_lane_off<D>(lane);
-  auto is_edge = [&](int j) { const int k0 = j * BC; return (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0); };
+  auto is_edge = [&](int j) { const int k0 = (t0 + j) * BC; return (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0); };
   uint32_t kvoff[KPlan::NPW], vvoff[VPlan::NPW];
   dma_init<KPlan, kWaves>(kvoff, row_bytes, wave, lane);
   dma_init<VPlan, kWaves>(vvoff, row_bytes, wave, lane);
   const char* kbase = (const char*)p.k + head_off;
   const char* vbase = (const char*)p.v + head_off;
-  auto dma_k = [&](int t) { dma_issue<KPlan, kWaves>(kvoff, kst(t), kbase, t * BC, row_bytes, nrec, wave); };
-  auto dma_v = [&](int t) { dma_issue<VPlan, kWaves>(vvoff, vst(t), vbase, t * BC, row_bytes, nrec, wave); };
+  auto dma_k = [&](int t) { dma_issue<KPlan, kWaves>(kvoff, kst(t), kbase, (t0 + t) * BC, row_bytes, nrec, wave); };
+  auto dma_v = [&](int t) { dma_issue<VPlan, kWaves>(vvoff, vst(t), vbase, (t0 + t) * BC, row_bytes, nrec, wave); };
 
   // Q^T operand: lane holds query q0 + l32, dims 16*ks + 8*hf .. +7.
   u32x4 qreg[NKS];
@@ -210,7 +227,7 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::WAVES, 1) void fwd_kernel(FwdParams
     for (int t = 1; t <= NS - 2; ++t) keep += (j + t < nkt ? nv_w : 0) + (j + t + 1 < nkt ? nk_w : 0);
     wait_dma_keep_rt<KEEP_MAX>(keep);
   };
-  dma_k(0);
+  if (nkt > 0) dma_k(0);   // a split-KV part can be empty: then no tile is loaded at all
 
   f32x16 oacc[NDB];
 #pragma unroll
@@ -233,7 +250,7 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::WAVES, 1) void fwd_kernel(FwdParams
   float mx_next = -INFINITY;
   if (nkt_w > 0) {
     tile_scores<BF16, D, NKB>(sc, kst(0) + k_lane, qreg);
-    if (is_edge(0)) tile_mask<CAUSAL, NKB>(sc, 0, N, qrow, hf);
+    if (is_edge(0)) tile_mask<CAUSAL, NKB>(sc, t0 * BC, N, qrow, hf);
     mx_next = tile_max<NKB>(sc, c);
   }
   // the first prefetch overwrites the stage of K(0), which the prologue just read
@@ -398,13 +415,34 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::WAVES, 1) void fwd_kernel(FwdParams
       tile_pv<BF16, D, NKB>(oacc, vst(j) + v_lane, pk);
       if (j + 1 < nkt_w) {
         tile_scores<BF16, D, NKB>(sc, kst(j + 1) + k_lane, qreg);
-        if (is_edge(j + 1)) tile_mask<CAUSAL, NKB>(sc, (j + 1) * BC, N, qrow, hf);
+        if (is_edge(j + 1)) tile_mask<CAUSAL, NKB>(sc, (t0 + j + 1) * BC, N, qrow, hf);
         mx_next = tile_max<NKB>(sc, c);
       }
     }
     end_tile(j);
   }
 
+  if (SPLIT && parts > 1) {
+    const size_t part = ((size_t)split * p.B + b) * H + h;   // [S][B][H]
+    if (qrow < N) {
+      if (nkt_w > 0) {
+        const float l_tot = xhalf_sum(l_run);
+        const float inv = 1.0f / l_tot;
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        float* orow = p.o_part + (part * N + qrow) * D;
+#pragma unroll
+        for (int i = 0; i < NDB; ++i)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            *(f32x4*)(orow + i * 32 + 8 * rr + 4 * hf) =
+                f32x4{oacc[i][4 * rr] * inv, oacc[i][4 * rr + 1] * inv, oacc[i][4 * rr + 2] * inv, oacc[i][4 * rr + 3] * inv};
+        if (hf == 0) p.lse_part[part * N + qrow] = (m_use + fast_log2(l_tot)) * kLn2;
+      } else if (hf == 0) {
+        p.lse_part[part * N + qrow] = -INFINITY;
+      }
+    }
+    return;
+  }
   if (nkt_w > 0) {
     const float l_tot = xhalf_sum(l_run);
     const float inv = 1.0f / l_tot;
@@ -420,6 +458,64 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::WAVES, 1) void fwd_kernel(FwdParams
       }
     if (hf == 0 && qrow < N) p.lse[((size_t)b * H + h) * N + qrow] = (m_use + fast_log2(l_tot)) * kLn2;
   }
+}
+
+// Merge of the split-KV parts, one row per D/8 threads (8 dims each): L = log sum_s e^{L_s},
+// O = sum_s e^{L_s - L} O_s over the parts of the row's query tile, parts with L_s = -inf
+// skipped (their O_s is never read). Rows of single-part tiles were written directly.
+constexpr int kMaxSplits = 16;
+template <bool BF16, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(FwdParams p) {
+  constexpr int TPR = D / 8;
+  constexpr int RPB = 256 / TPR;
+  const int H = p.H, N = p.N;
+  const size_t rows = (size_t)p.B * H * N;
+  const size_t row = (size_t)blockIdx.x * RPB + threadIdx.x / TPR;   // (b, h, n) order
+  const int c = threadIdx.x % TPR;
+  if (row >= rows) return;
+  const int n = (int)(row % N);
+  const int qt = n / fwd_rows<D>();
+  const int kend = CAUSAL ? min(N, (qt + 1) * fwd_rows<D>()) : N;
+  const int nkt_all = (kend + FwdCfg<D>::BC - 1) / FwdCfg<D>::BC;
+  const int S = (nkt_all + p.split_tiles - 1) / p.split_tiles;
+  if (S <= 1) return;
+  const size_t bh = row / N;
+  const int h = (int)(bh % H), b = (int)(bh / H);
+  float m = -INFINITY;
+  for (int s = 0; s < S; ++s) m = fmaxf(m, p.lse_part[(size_t)s * rows + row]);
+  float sum = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < S; ++s) {
+    const float ls = p.lse_part[(size_t)s * rows + row];
+    if (ls == -INFINITY) continue;
+    const float w = __expf(ls - m);
+    sum += w;
+    const f32x4* src = (const f32x4*)(p.o_part + ((size_t)s * rows + row) * D + 8 * c);
+    const f32x4 lo = src[0], hi = src[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] += w * lo[e];
+      acc[4 + e] += w * hi[e];
+    }
+  }
+  const float inv = 1.0f / sum;
+  const u32x4 out = {pack2<BF16>(acc[0] * inv, acc[1] * inv), pack2<BF16>(acc[2] * inv, acc[3] * inv),
+                     pack2<BF16>(acc[4] * inv, acc[5] * inv), pack2<BF16>(acc[6] * inv, acc[7] * inv)};
+  *(u32x4*)((char*)p.o + ((((size_t)b * N + n) * H + h) * D + 8 * c) * 2) = out;
+  if (c == 0) p.lse[row] = m + __logf(sum);
+}
+
+template <bool BF16, int D, bool CAUSAL>
+hipError_t launch_split(const FwdParams& p, hipStream_t s) {
+  static_assert(FwdCfg<D>::BC == 64, "split_tiles is computed for 64-key tiles");
+  const int nqt = (p.N + fwd_rows<D>() - 1) / fwd_rows<D>();
+  const dim3 grid((unsigned)(p.B * p.H * nqt * p.splits));
+  hipLaunchKernelGGL((fwd_kernel<BF16, D, CAUSAL, true>), grid, dim3(64 * FwdCfg<D>::WAVES), 0, s, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int RPB = 256 / (D / 8);
+  const size_t rows = (size_t)p.B * p.H * p.N;
+  hipLaunchKernelGGL((fwd_merge_kernel<BF16, D, CAUSAL>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 
 template <bool BF16, int D, bool CAUSAL>
@@ -449,6 +545,24 @@ hipError_t launch_d(int d, bool causal, const FwdParams& p, hipStream_t s) {
 
 hipError_t launch_fwd(bool bf16, int d, bool causal, const FwdParams& p, hipStream_t s) {
   return bf16 ? launch_d<true>(d, causal, p, s) : launch_d<false>(d, causal, p, s);
+}
+
+template <bool BF16>
+hipError_t launch_split_d(int d, bool causal, const FwdParams& p, hipStream_t s) {
+  switch (d) {
+    case 64: return causal ? launch_split<BF16, 64, true>(p, s) : launch_split<BF16, 64, false>(p, s);
+    case 128: return causal ? launch_split<BF16, 128, true>(p, s) : launch_split<BF16, 128, false>(p, s);
+    case 256: return causal ? launch_split<BF16, 256, true>(p, s) : launch_split<BF16, 256, false>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_fwd_splitkv(bool bf16, int d, bool causal, const FwdParams& p, hipStream_t s) {
+  if (p.splits < 1 || p.splits > kMaxSplits) return hipErrorInvalidValue;
+  FwdParams q = p;
+  const int nkt_max = (p.N + 63) / 64;   // key tiles of the longest query tile (BC = 64)
+  q.split_tiles = (nkt_max + p.splits - 1) / p.splits;
+  return bf16 ? launch_split_d<true>(d, causal, q, s) : launch_split_d<false>(d, causal, q, s);
 }
 
 }  // namespace attn

@@ -13,6 +13,14 @@ struct FwdParams {
   float* lse;
   int B, H, N;
   float c;  // softmax scale * log2(e): scores are exponentiated with exp2
+  // split-KV only: S = splits part slots per query tile; a query tile with n key tiles
+  // uses ceil(n / split_tiles) of them (split_tiles = ceil(ceil(N/64) / S)); the per-part
+  // results O_s = O/l (fp32 [S][B][H][N][d]) and L_s (fp32 [S][B][H][N]; -inf: no keys of
+  // the row in the part). A query tile with one part writes o and lse directly.
+  int splits;
+  float* o_part;
+  float* lse_part;
+  int split_tiles;
 };
 
 struct BwdParams {
@@ -55,6 +63,8 @@ struct Fp8FwdParams {
 };
 
 hipError_t launch_fwd(bool bf16, int d, bool causal, const FwdParams& p, hipStream_t s);
+// the split-KV forward, then the merge of its parts into p.o and p.lse
+hipError_t launch_fwd_splitkv(bool bf16, int d, bool causal, const FwdParams& p, hipStream_t s);
 hipError_t launch_bwd(bool bf16, int d, bool causal, const BwdParams& p, hipStream_t s);
 hipError_t launch_fp8_quantize(bool bf16, int d, const Fp8QuantParams& p, hipStream_t s);
 hipError_t launch_fwd_fp8(bool out_bf16, int d, bool causal, const Fp8FwdParams& p, hipStream_t s);

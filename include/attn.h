@@ -54,6 +54,26 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, flo
                        int B, int H, int N, int d, int causal, float scale,
                        attn_dtype_t dtype, attn_stream_t stream);
 
+/* Bytes of device workspace attn_fwd_splitkv needs: per part, O_s fp32 [B][H][N][d] and
+ * L_s fp32 [B][H][N] (num_splits * B*H*N*(d+1) * 4 bytes). 0 for invalid arguments. */
+size_t attn_fwd_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits);
+
+/* Forward exact attention with the key range split: the results of attn_fwd (up to
+ * rounding), for problems too small to fill the GPU one query tile per workgroup (short N,
+ * few heads). Each query tile's key tiles are cut into num_splits contiguous parts
+ * (1 <= num_splits <= 16) that separate workgroups process; part s yields O_s = O/l and
+ * L_s over its keys, and a merge forms L = log sum_s exp(L_s) and O = sum_s exp(L_s - L) O_s
+ * (the log-sum-exp state of the online softmax, Symbol Map: m_i, l_i, L_i; the same merge
+ * that joins sequence shards in ring attention, enterprise post "Million-Token Context
+ * Windows"). Parts with no key for a row (causal) are skipped. `workspace` must hold
+ * attn_fwd_splitkv_workspace_bytes(...) bytes; contents on entry are ignored, on return
+ * unspecified. Errors as attn_fwd, plus ATTN_EINVAL for num_splits out of range and
+ * ATTN_EWORKSPACE. */
+attn_status_t attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int H, int N, int d, int causal, float scale,
+                               attn_dtype_t dtype, int num_splits, void* workspace,
+                               size_t workspace_bytes, attn_stream_t stream);
+
 /* Bytes of device workspace attn_bwd needs: fp32 D = rowsum(dO o O), [B][H][N]. */
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
 

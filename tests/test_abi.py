@@ -60,6 +60,12 @@ def test_null_pointers_rejected(lib):
                         None, 0, None) == 1
     assert lib.attn_fp8_quantize(None, None, None, 1, 1, 16, 64, 0, 1, 0, None) == 1
     assert lib.attn_fp8_quantize_per_tensor(None, None, None, 1, 1, 16, 64, 0, 1, 0, None) == 1
+    assert lib.attn_fwd_splitkv(None, None, None, None, None, 1, 1, 16, 64, 0, 0.125, 0, 2, None, 0, None) == 1
+    assert lib.attn_fwd_splitkv(None, None, None, None, None, 1, 1, 16, 64, 0, 0.125, 0, 0, None, 0, None) == 1
+    assert lib.attn_fwd_splitkv(None, None, None, None, None, 1, 1, 16, 96, 0, 0.125, 0, 2, None, 0, None) == 2
+    assert lib.attn_fwd_splitkv_workspace_bytes(1, 2, 100, 64, 3) == 3 * 2 * 100 * 65 * 4
+    assert lib.attn_fwd_splitkv_workspace_bytes(1, 2, 100, 64, 17) == 0
+    assert lib.attn_fwd_splitkv_workspace_bytes(1, 2, 100, 96, 2) == 0
     assert lib.attn_fp8_quantize_per_tensor(None, None, None, 1, 1, 16, 100, 0, 1, 0, None) == 2
     assert lib.attn_fwd_fp8(None, None, None, None, None, 1, 1, 16, 64, 0, 0.125, None, None, None, 0, 0,
                             None) == 1
