@@ -153,26 +153,30 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
   const int qt0 = CAUSAL ? (kt * BKV) / BQ : 0;
   uint32_t qvoff[QPlan::NPW];
   dma_init<QPlan, kWaves, SWZ>(qvoff, row_bytes, wave, lane);
-  float lval = 0.f, dval = 0.f;   // L (log2 domain) and D of query row (tile start + tid), tid < BQ
+  // L and D of query row (tile start + tid), tid < BQ: loaded one tile before they are staged
+  // into LDS, and used (scaled, masked past the end) only then. Any arithmetic on them at
+  // the load would make the wave wait there for the load and for the tile DMA issued just
+  // before it (the counter is in order).
+  float lraw = 0.f, draw = 0.f;
   auto load_ld = [&](int qt) {
     if (tid < BQ) {
-      const int q = qt * BQ + tid;
-      lval = q < N ? lse_h[q] * kLog2e : INFINITY;   // P = exp2(s*c - inf) = 0 past the end
-      dval = q < N ? del_h[q] : 0.f;
+      const int q = min(qt * BQ + tid, N - 1);   // in bounds; rows past the end are masked when staged
+      lraw = lse_h[q];
+      draw = del_h[q];
     }
   };
-  auto fetch = [&](int qt, int stage) {
-    char* st = smem + stage * STAGE;
+  auto fetch_into = [&](int qt, char* st) {
     if (tid < BQ) {
-      ((float*)(st + OFF_L))[tid] = lval;
-      ((float*)(st + OFF_D))[tid] = dval;
+      const bool in = qt * BQ + tid < N;
+      ((float*)(st + OFF_L))[tid] = in ? lraw * kLog2e : INFINITY;   // P = exp2(s*c - inf) = 0 past the end
+      ((float*)(st + OFF_D))[tid] = in ? draw : 0.f;
     }
     dma_issue<QPlan, kWaves>(qvoff, st, qbase, qt * BQ, row_bytes, nrec, wave);
     dma_issue<QPlan, kWaves>(qvoff, st + OFF_DO, dobase, qt * BQ, row_bytes, nrec, wave);
   };
   if (qt0 < nqt) {
     load_ld(qt0);
-    fetch(qt0, 0);
+    fetch_into(qt0, smem);
     if (qt0 + 1 < nqt) load_ld(qt0 + 1);
   }
 
@@ -336,21 +340,28 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
   // waves whose keys all follow the tile skip it; the rest need neither. Two loops keep each
   // loop body straight-line (one tile form, no skip branch), so the accumulators stay put.
   // Waves past the end of the sequence compute on zero-filled K, V and store nothing.
-  auto step = [&](int qt, auto edge_tag) {
+  // One Q tile: DMA of the next tile into stage `nxt` and the math on stage `cur`. The two
+  // stages are distinct, and saying so (restrict) lets the compiler see that the tile's LDS
+  // reads cannot alias the DMA in flight: otherwise it waits for that DMA before the first
+  // transpose read of the tile.
+  auto body = [&](int qt, char* __restrict__ nxt, const char* __restrict__ cur, auto edge_tag) {
     constexpr bool EDGE = decltype(edge_tag)::value;
-    pin_all();
-    const int i = qt - qt0;
     if (qt + 1 < nqt) {
-      fetch(qt + 1, (i + 1) & 1);
+      fetch_into(qt + 1, nxt);
       if (qt + 2 < nqt) load_ld(qt + 2);
     }
     const int q0 = qt * BQ;
-    const char* st = smem + __builtin_amdgcn_readfirstlane((i & 1) * STAGE);
     if constexpr (EDGE) {
-      if (wave_live && q0 + BQ - 1 >= k0w) tile(st, q0, std::true_type{});
+      if (wave_live && q0 + BQ - 1 >= k0w) tile(cur, q0, std::true_type{});
     } else {
-      tile(st, q0, std::false_type{});
+      tile(cur, q0, std::false_type{});
     }
+  };
+  auto step = [&](int qt, auto edge_tag) {
+    pin_all();
+    const int i = qt - qt0;
+    const int cur = __builtin_amdgcn_readfirstlane((i & 1) * STAGE);
+    body(qt, smem + (STAGE - cur), smem + cur, edge_tag);
     wait_dma();
     __syncthreads();
     pin_all();
@@ -432,12 +443,11 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(BwdParams p)
   uint32_t kvoff[KPlan::NPW], vvoff[VPlan::NPW];
   dma_init<KPlan, kWaves, SWZ>(kvoff, row_bytes, wave, lane);
   dma_init<VPlan, kWaves>(vvoff, row_bytes, wave, lane);
-  auto fetch = [&](int j) {
-    char* st = smem + (j & 1) * STAGE;
+  auto fetch_into = [&](int j, char* st) {
     dma_issue<KPlan, kWaves>(kvoff, st, kbase, j * BC, row_bytes, nrec, wave);
     dma_issue<VPlan, kWaves>(vvoff, st + KB, vbase, j * BC, row_bytes, nrec, wave);
   };
-  fetch(0);
+  fetch_into(0, smem);
 
   u32x4 qreg[NKS], doreg[NKS];
 #pragma unroll
@@ -478,9 +488,8 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(BwdParams p)
   constexpr int S1 = NKB * NKS;            // MFMAs per score product
   constexpr int EPS = 16 * NKB / S1;       // exponentials per dP step
   constexpr int PF = 3;
-  auto tile = [&](int j, auto edge_tag) {
+  auto tile = [&](int j, const char* st, auto edge_tag) {
     constexpr bool EDGE = decltype(edge_tag)::value;
-    const char* st = smem + (j & 1) * STAGE;
     const char* vr = st + KB + row_v;
     const int k0 = j * BC;
     f32x16 s[NKB], dp[NKB];
@@ -540,13 +549,20 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(BwdParams p)
     }
   };
 
-  for (int j = 0; j < nkt; ++j) {
-    if (j + 1 < nkt) fetch(j + 1);
+  // DMA of the next tile into stage `nxt` and the math on stage `cur`: distinct stages,
+  // passed as restrict pointers so that the tile's LDS reads are not made to wait for the
+  // DMA in flight (the wait at the end of the iteration covers the next tile).
+  auto body = [&](int j, char* __restrict__ nxt, const char* __restrict__ cur) {
+    if (j + 1 < nkt) fetch_into(j + 1, nxt);
     if (j < nkt_w) {
       const int k0 = j * BC;
-      if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0)) tile(j, std::true_type{});
-      else tile(j, std::false_type{});
+      if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0)) tile(j, cur, std::true_type{});
+      else tile(j, cur, std::false_type{});
     }
+  };
+  for (int j = 0; j < nkt; ++j) {
+    const int cur = (j & 1) * STAGE;
+    body(j, smem + (STAGE - cur), smem + cur);
     wait_dma();
     __syncthreads();
   }
