@@ -15,6 +15,10 @@ Readings where the pages are silent:
   * log base of L: natural log, as written in the Symbol Map.
   * causal mask: key j is visible to query i iff j <= i (equal query and key lengths).
   * layout: tensors are [B, N, H, d] (token-major); L is [B, H, N].
+  * grouped-query attention: the enterprise post ("FlashAttention 3 Hardware Acceleration",
+    section "Runtime Kernel Selection") names the pattern without a formula. Reading: K and V
+    may have Hkv heads, Hkv dividing H; query head h reads key/value head h // (H / Hkv); a
+    shared head's dK, dV are the sums of the gradients through each of its query heads.
 
 Row blocks below only bound memory: each row's softmax still sees its full key set at once,
 and dK/dV sum over query rows block by block (the same sum, grouped).
@@ -22,7 +26,9 @@ and dK/dV sum over query rows block by block (the same sum, grouped).
 Pins (tests/test_oracle_attention.py): torch's fp64 CPU math attention and autograd,
 scipy's logsumexp/softmax, central finite differences, invariants (rows of P sum to 1,
 constant V, key permutation, sum of dK = 0, sum of dV = sum of dO), closed forms (one-hot
-scores, scale = 0, N = 1, causal row 0) and the split-KV log-sum-exp merge identity.
+scores, scale = 0, N = 1, causal row 0) and the split-KV log-sum-exp merge identity; for
+grouped key/value heads, torch's fp64 grouped-query attention and its autograd, and central
+finite differences through a shared head.
 """
 import numpy as np
 
@@ -84,22 +90,33 @@ def head_forward(qh, kh, vh, causal=False, scale=None, rows=None):
     return o, lse
 
 
+def kv_head(h, H, Hkv):
+    """Key/value head read by query head h when Hkv heads are shared by groups of H/Hkv
+    consecutive query heads (grouped-query attention; Hkv = H is ordinary attention)."""
+    if Hkv <= 0 or H % Hkv:
+        raise ValueError(f"{H} query heads cannot be grouped over {Hkv} key/value heads")
+    return h // (H // Hkv)
+
+
 def forward(q, k, v, causal=False, scale=None):
-    """Batched forward over [B, N, H, d]. Returns O [B, N, H, d] and L [B, H, N] in fp64."""
+    """Batched forward: q [B, N, H, d], k and v [B, N, Hkv, d] with Hkv dividing H (query
+    head h attends to key/value head kv_head(h)). Returns O [B, N, H, d] and L [B, H, N]."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, N, H, d = q.shape
+    Hkv = k.shape[2]
     o = np.empty((B, N, H, v.shape[3]))
     lse = np.empty((B, H, N))
     for b in range(B):
         for h in range(H):
-            o[b, :, h], lse[b, h] = head_forward(q[b, :, h], k[b, :, h], v[b, :, h], causal, scale)
+            g = kv_head(h, H, Hkv)
+            o[b, :, h], lse[b, h] = head_forward(q[b, :, h], k[b, :, g], v[b, :, g], causal, scale)
     return o, lse
 
 
 def forward_rows(q, k, v, b, h, rows, causal=False, scale=None):
     """O and L for selected query rows of head (b, h); used for sampled checks at full size."""
-    q, k, v = (x[b, :, h] for x in (q, k, v))
-    return head_forward(q, k, v, causal, scale, rows=np.asarray(rows))
+    g = kv_head(h, q.shape[2], k.shape[2])
+    return head_forward(q[b, :, h], k[b, :, g], v[b, :, g], causal, scale, rows=np.asarray(rows))
 
 
 def head_backward(qh, kh, vh, doh, causal=False, scale=None):
@@ -128,14 +145,19 @@ def head_backward(qh, kh, vh, doh, causal=False, scale=None):
 
 
 def backward(q, k, v, do, causal=False, scale=None):
-    """Batched gradients over [B, N, H, d]; returns fp64 (dQ, dK, dV)."""
+    """Batched gradients; shapes as in forward. A shared key/value head collects the
+    gradients of every query head that reads it. Returns fp64 (dQ, dK, dV)."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, N, H, d = q.shape
-    dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    Hkv = k.shape[2]
+    dq, dk, dv = np.empty_like(q), np.zeros_like(k), np.zeros_like(v)
     for b in range(B):
         for h in range(H):
-            dq[b, :, h], dk[b, :, h], dv[b, :, h] = head_backward(
-                q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], causal, scale)
+            g = kv_head(h, H, Hkv)
+            dqh, dkh, dvh = head_backward(q[b, :, h], k[b, :, g], v[b, :, g], do[b, :, h], causal, scale)
+            dq[b, :, h] = dqh
+            dk[b, :, g] += dkh
+            dv[b, :, g] += dvh
     return dq, dk, dv
 
 

@@ -210,6 +210,54 @@ def test_rowsum_identity_used_by_gradient_kernels():
         np.testing.assert_allclose((p * (do @ v.T)).sum(1), (do * o).sum(1), atol=1e-12)
 
 
+@pytest.mark.parametrize("hkv", [1, 2])
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_kv_heads_match_torch(hkv, causal):
+    """Grouped-query attention against torch's fp64 implementation (enable_gqa) and its
+    autograd: forward O and the gradients of the shared key/value heads."""
+    B, N, H, d, sc = 2, 37, 4, 8, 0.7
+    q, do = _rand(B, N, H, d), _rand(B, N, H, d)
+    k, v = _rand(B, N, hkv, d), _rand(B, N, hkv, d)
+    tq, tk, tv = (torch.from_numpy(x).permute(0, 2, 1, 3).contiguous().requires_grad_(True) for x in (q, k, v))
+    o_t = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=sc, enable_gqa=True)
+    o_t.backward(torch.from_numpy(do).permute(0, 2, 1, 3))
+    o, _ = oracle.forward(q, k, v, causal, sc)
+    np.testing.assert_allclose(o, o_t.detach().permute(0, 2, 1, 3).numpy(), atol=1e-12)
+    dq, dk, dv = oracle.backward(q, k, v, do, causal, sc)
+    assert dk.shape == k.shape and dv.shape == v.shape
+    for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(mine, ref.permute(0, 2, 1, 3).numpy(), atol=1e-12)
+
+
+def test_grouped_kv_heads_finite_differences():
+    """dK and dV of a key/value head shared by two query heads, by central differences of
+    sum(dO o O) over all heads."""
+    B, N, H, hkv, d, sc, h = 1, 5, 4, 2, 4, 0.8, 1e-6
+    q, do = _rand(B, N, H, d), _rand(B, N, H, d)
+    k, v = _rand(B, N, hkv, d), _rand(B, N, hkv, d)
+    for causal in (False, True):
+        _, dk, dv = oracle.backward(q, k, v, do, causal, sc)
+
+        def loss(kk, vv):
+            return float((oracle.forward(q, kk, vv, causal, sc)[0] * do).sum())
+
+        for which, grad in ((0, dk), (1, dv)):
+            fd = np.empty_like(grad)
+            for idx in np.ndindex(*grad.shape):
+                ap, am = [k.copy(), v.copy()], [k.copy(), v.copy()]
+                ap[which][idx] += h
+                am[which][idx] -= h
+                fd[idx] = (loss(*ap) - loss(*am)) / (2 * h)
+            assert np.abs(fd - grad).max() <= 1e-6 * np.abs(grad).max(), (causal, which)
+
+
+def test_kv_head_mapping():
+    assert [oracle.kv_head(h, 8, 2) for h in range(8)] == [0, 0, 0, 0, 1, 1, 1, 1]
+    assert [oracle.kv_head(h, 4, 4) for h in range(4)] == [0, 1, 2, 3]
+    with pytest.raises(ValueError):
+        oracle.kv_head(0, 6, 4)
+
+
 def test_flop_convention():
     assert oracle.flops_forward(2, 16, 8192, 128, False) == 4 * 2 * 16 * 8192 ** 2 * 128
     assert oracle.flops_forward(2, 16, 8192, 128, True) == 2 * 2 * 16 * 8192 ** 2 * 128

@@ -65,7 +65,12 @@ def _bwd_d_sign(qh, kh, vh, doh, causal=False, scale=None):
     return sc * ds @ kh, sc * ds.T @ qh, p.T @ doh
 
 
+def _kv_head_interleaved(h, H, Hkv):
+    return h % Hkv
+
+
 ATTN_CASES = {
+    "grouped heads interleaved": ("kv_head", _kv_head_interleaved),
     "flipped causal mask": ("_scores", _scores_flipped_mask),
     "dropped scale": ("_scores", _scores_no_scale),
     "log2 lse": ("head_forward", _fwd_log2),
@@ -83,6 +88,7 @@ def _attention_pins():
         (TA.test_backward_matches_torch_autograd, (1, 33, 3, 16), True),
         (TA.test_backward_matches_torch_autograd, (2, 5, 2, 8), False),
         (TA.test_backward_finite_differences, 8, 8, True),
+        (TA.test_grouped_kv_heads_match_torch, 2, True),
     ]
 
 
