@@ -19,8 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libattn.so")
 
 ATTN_BF16, ATTN_FP16 = 0, 1
 FP8_BLOCK = 64
-EXPORTS = ("attn_fwd", "attn_fwd_splitkv_workspace_bytes", "attn_fwd_splitkv",
-           "attn_bwd_workspace_bytes", "attn_bwd", "attn_fp8_quantize",
+EXPORTS = ("attn_fwd", "attn_fwd_gqa", "attn_fwd_splitkv_workspace_bytes", "attn_fwd_splitkv",
+           "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_gqa", "attn_fp8_quantize",
            "attn_fp8_quantize_per_tensor", "attn_fwd_fp8", "attn_strerror")
 _DTYPE_CODE = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_FP16}
 
@@ -45,6 +45,8 @@ def load(path=None):
     vp, i, f, sz, u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_uint64
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     L.attn_fwd.restype = i
+    L.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    L.attn_fwd_gqa.restype = i
     L.attn_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
     L.attn_fwd_splitkv_workspace_bytes.restype = sz
     L.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
@@ -53,6 +55,8 @@ def load(path=None):
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     L.attn_bwd.restype = i
+    L.attn_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
+    L.attn_bwd_gqa.restype = i
     for fn in (L.attn_fp8_quantize, L.attn_fp8_quantize_per_tensor):
         fn.argtypes = [vp, vp, vp, i, i, i, i, i, i, u64, vp]
         fn.restype = i
@@ -114,6 +118,50 @@ def attn_fwd(q, k, v, causal=False, scale=None, o=None, lse=None, stream=None):
                                        int(bool(causal)), _default_scale(d, scale), _DTYPE_CODE[q.dtype],
                                        _stream(q, stream)))
     return o, lse
+
+
+def attn_fwd_gqa(q, k, v, causal=False, scale=None, o=None, lse=None, stream=None):
+    """Grouped-query forward: q [B, N, H, d]; k, v [B, N, H_kv, d] with H_kv dividing H."""
+    _tensor(q, "q", dtypes=tuple(_DTYPE_CODE))
+    B, N, H, d = q.shape
+    _tensor(k, "k", dtypes=(q.dtype,), device=q.device)
+    hkv = k.shape[2] if k.dim() == 4 else 0
+    _tensor(k, "k", (B, N, hkv, d), (q.dtype,), q.device)
+    _tensor(v, "v", (B, N, hkv, d), (q.dtype,), q.device)
+    o = torch.empty_like(q) if o is None else _tensor(o, "o", q.shape, (q.dtype,), q.device)
+    lse = (torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None
+           else _tensor(lse, "lse", (B, H, N), (torch.float32,), q.device))
+    _check("attn_fwd_gqa", load().attn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, hkv, N, d,
+                                               int(bool(causal)), _default_scale(d, scale), _DTYPE_CODE[q.dtype],
+                                               _stream(q, stream)))
+    return o, lse
+
+
+def attn_bwd_gqa(q, k, v, o, lse, do, causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None,
+                 stream=None):
+    """Grouped-query backward: shapes as attn_fwd_gqa; dk, dv have H_kv heads."""
+    _tensor(q, "q", dtypes=tuple(_DTYPE_CODE))
+    B, N, H, d = q.shape
+    _tensor(k, "k", dtypes=(q.dtype,), device=q.device)
+    hkv = k.shape[2] if k.dim() == 4 else 0
+    kv_shape = (B, N, hkv, d)
+    _tensor(k, "k", kv_shape, (q.dtype,), q.device)
+    _tensor(v, "v", kv_shape, (q.dtype,), q.device)
+    for name, t in (("o", o), ("do", do)):
+        _tensor(t, name, q.shape, (q.dtype,), q.device)
+    _tensor(lse, "lse", (B, H, N), (torch.float32,), q.device)
+    dq = torch.empty_like(q) if dq is None else _tensor(dq, "dq", q.shape, (q.dtype,), q.device)
+    dk = torch.empty_like(k) if dk is None else _tensor(dk, "dk", kv_shape, (q.dtype,), q.device)
+    dv = torch.empty_like(v) if dv is None else _tensor(dv, "dv", kv_shape, (q.dtype,), q.device)
+    need = attn_bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _tensor(workspace, "workspace", device=q.device)
+    _check("attn_bwd_gqa", load().attn_bwd_gqa(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), B, H, hkv, N, d,
+        int(bool(causal)), _default_scale(d, scale), _DTYPE_CODE[q.dtype], _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q, stream)))
+    return dq, dk, dv
 
 
 def attn_fwd_splitkv_workspace_bytes(B, H, N, d, num_splits):

@@ -60,19 +60,33 @@ uint64_t splitmix64_output(uint64_t seed, uint64_t t) {
 
 extern "C" {
 
-attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                       int B, int H, int N, int d, int causal, float scale,
-                       attn_dtype_t dtype, attn_stream_t stream) {
+static attn_status_t fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int H, int Hkv, int N, int d, int causal, float scale,
+                                attn_dtype_t dtype, attn_stream_t stream) {
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_EINVAL;
   if (bad_scale(scale)) return ATTN_EINVAL;
   bool empty = false;
   attn_status_t st = check_sizes(B, H, N, d, &empty);
-  if (st != ATTN_OK || empty) return st;
+  if (st != ATTN_OK) return st;
+  if (Hkv < 1 || (H > 0 && H % Hkv != 0)) return ATTN_EINVAL;
+  if (empty) return ATTN_OK;
   if (!q || !k || !v || !o || !lse) return ATTN_EINVAL;
   if ((st = check_device()) != ATTN_OK) return st;
-  attn::FwdParams p{q, k, v, o, lse, B, H, N, (float)(scale * kLog2e)};
+  attn::FwdParams p{q, k, v, o, lse, B, H, N, (float)(scale * kLog2e), Hkv};
   (void)hipGetLastError();
   return launched(attn::launch_fwd(dtype == ATTN_BF16, d, causal != 0, p, (hipStream_t)stream));
+}
+
+attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int N, int d, int causal, float scale,
+                       attn_dtype_t dtype, attn_stream_t stream) {
+  return fwd_common(q, k, v, o, lse, B, H, H > 0 ? H : 1, N, d, causal, scale, dtype, stream);
+}
+
+attn_status_t attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int H_kv, int N, int d, int causal, float scale,
+                           attn_dtype_t dtype, attn_stream_t stream) {
+  return fwd_common(q, k, v, o, lse, B, H, H_kv, N, d, causal, scale, dtype, stream);
 }
 
 size_t attn_fwd_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits) {
@@ -98,7 +112,7 @@ attn_status_t attn_fwd_splitkv(const void* q, const void* k, const void* v, void
     return ATTN_EWORKSPACE;
   if ((st = check_device()) != ATTN_OK) return st;
   float* ws = (float*)workspace;
-  attn::FwdParams p{q, k, v, o, lse, B, H, N, (float)(scale * kLog2e), num_splits, ws,
+  attn::FwdParams p{q, k, v, o, lse, B, H, N, (float)(scale * kLog2e), H, num_splits, ws,
                     ws + (size_t)num_splits * B * H * N * d};
   (void)hipGetLastError();
   return launched(attn::launch_fwd_splitkv(dtype == ATTN_BF16, d, causal != 0, p, (hipStream_t)stream));
@@ -110,23 +124,43 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N, int d) {
   return (size_t)B * H * N * sizeof(float);
 }
 
+static attn_status_t bwd_common(const void* q, const void* k, const void* v, const void* o,
+                                const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                int B, int H, int Hkv, int N, int d, int causal, float scale,
+                                attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                attn_stream_t stream) {
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_EINVAL;
+  if (bad_scale(scale)) return ATTN_EINVAL;
+  bool empty = false;
+  attn_status_t st = check_sizes(B, H, N, d, &empty);
+  if (st != ATTN_OK) return st;
+  if (Hkv < 1 || (H > 0 && H % Hkv != 0)) return ATTN_EINVAL;
+  if (empty) return ATTN_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_EINVAL;
+  if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, H, N, d)) return ATTN_EWORKSPACE;
+  if ((st = check_device()) != ATTN_OK) return st;
+  attn::BwdParams p{q, k, v, o, lse, dout, dq, dk, dv, (float*)workspace, B, H, N, scale,
+                    (float)(scale * kLog2e), Hkv};
+  (void)hipGetLastError();
+  return launched(attn::launch_bwd(dtype == ATTN_BF16, d, causal != 0, p, (hipStream_t)stream));
+}
+
 attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o,
                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
                        int B, int H, int N, int d, int causal, float scale,
                        attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
                        attn_stream_t stream) {
-  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_EINVAL;
-  if (bad_scale(scale)) return ATTN_EINVAL;
-  bool empty = false;
-  attn_status_t st = check_sizes(B, H, N, d, &empty);
-  if (st != ATTN_OK || empty) return st;
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_EINVAL;
-  if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, H, N, d)) return ATTN_EWORKSPACE;
-  if ((st = check_device()) != ATTN_OK) return st;
-  attn::BwdParams p{q, k, v, o, lse, dout, dq, dk, dv, (float*)workspace, B, H, N, scale,
-                    (float)(scale * kLog2e)};
-  (void)hipGetLastError();
-  return launched(attn::launch_bwd(dtype == ATTN_BF16, d, causal != 0, p, (hipStream_t)stream));
+  return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, B, H, H > 0 ? H : 1, N, d, causal, scale, dtype,
+                    workspace, workspace_bytes, stream);
+}
+
+attn_status_t attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           int B, int H, int H_kv, int N, int d, int causal, float scale,
+                           attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                           attn_stream_t stream) {
+  return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, d, causal, scale, dtype,
+                    workspace, workspace_bytes, stream);
 }
 
 static attn_status_t fp8_quantize(const void* x, uint8_t* x8, float* descale, int B, int H, int N,

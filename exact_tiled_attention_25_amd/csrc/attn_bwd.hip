@@ -9,7 +9,9 @@
 //
 // gfx950 design. Three kernels on the caller's stream, no atomics (deterministic):
 //  1. bwd_pre:  D = rowsum(dO o O) in fp32 into the workspace (HBM-bound, one pass).
-//  2. bwd_dkdv: one workgroup per 128 keys of a head (4 waves x 32 keys). Each wave keeps
+//  2. bwd_dkdv: one workgroup per 128 keys of a key/value head (4 waves x 32 keys); with
+//     grouped key/value heads it visits the Q tiles of every query head of the group, so
+//     dK and dV are summed in registers (no atomics). Each wave keeps
 //     its keys' K and V in registers as MFMA B operands and its dK^T, dV^T accumulators in
 //     registers; Q and dO tiles stream through a two-stage LDS ring in both row-major (for
 //     S = Q K^T and dP = dO V^T) and transposed (for dV^T += dO^T P, dK^T += Q^T dS) form.
@@ -128,29 +130,44 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps loop control scalar
   const int l32 = lane & 31, hf = lane >> 5;
-  const int H = p.H, N = p.N;
+  const int H = p.H, N = p.N, Hkv = p.Hkv, G = H / Hkv;
   const int nkvt = (N + BKV - 1) / BKV;
   const int work = xcd_remap(blockIdx.x, gridDim.x);
   const int kt = work % nkvt;          // causal: low key tiles see the most queries; they go first
   const int bh = work / nkvt;
-  const int h = bh % H, b = bh / H;
+  const int kvh = bh % Hkv, b = bh / Hkv;   // key/value head; its query heads are kvh*G .. +G-1
   const int k0w = kt * BKV + wave * 32;
   const int key = k0w + l32;
 
+  // K, V, dK, dV: [B][N][Hkv][D]; Q, dO: [B][N][H][D]; L, D: [B][H][N]
+  const uint32_t kv_row_bytes = (uint32_t)Hkv * D * 2;
+  const size_t kv_head_off = ((size_t)b * N * Hkv + kvh) * D * 2;
+  const uint32_t kv_nrec = (uint32_t)N * kv_row_bytes - (uint32_t)kvh * D * 2;
+  const auto rk = make_rsrc((const char*)p.k + kv_head_off, kv_nrec);
+  const auto rv = make_rsrc((const char*)p.v + kv_head_off, kv_nrec);
+  const auto rdk = make_rsrc((const char*)p.dk + kv_head_off, kv_nrec);
+  const auto rdv = make_rsrc((const char*)p.dv + kv_head_off, kv_nrec);
   const uint32_t row_bytes = (uint32_t)H * D * 2;
-  const size_t head_off = ((size_t)b * N * H + h) * D * 2;
-  const uint32_t nrec = (uint32_t)N * row_bytes - (uint32_t)h * D * 2;
-  const auto rk = make_rsrc((const char*)p.k + head_off, nrec);
-  const auto rv = make_rsrc((const char*)p.v + head_off, nrec);
-  const auto rdk = make_rsrc((const char*)p.dk + head_off, nrec);
-  const auto rdv = make_rsrc((const char*)p.dv + head_off, nrec);
-  const char* qbase = (const char*)p.q + head_off;
-  const char* dobase = (const char*)p.dout + head_off;
-  const float* lse_h = p.lse + ((size_t)b * H + h) * N;
-  const float* del_h = p.delta + ((size_t)b * H + h) * N;
 
   const int nqt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? (kt * BKV) / BQ : 0;
+  // The workgroup visits query tiles qt0 .. nqt-1 of each of its G query heads. Causal: the
+  // tiles before qe reach this workgroup's keys and need the mask. Order (u numbers it): the
+  // masked tiles of every head, then the plain tiles of every head; two straight-line loops,
+  // as dK and dV are sums in any order.
+  // Positions advance by compares only (a division here would be scheduled into the tile
+  // body, where every register is taken).
+  const int qe = CAUSAL ? max(qt0, min(nqt, (kt * BKV + BKV - 1 + BQ - 1) / BQ)) : qt0;
+  const int UE = G * (qe - qt0), NU = G * (nqt - qt0);
+  struct Pos { int g, qt; };   // query head kvh*G + g, query tile qt
+  auto first_pos = [&]() { return qe > qt0 ? Pos{0, qt0} : Pos{0, qe}; };
+  auto next_pos = [&](Pos q) {
+    if (q.qt < qe) {   // masked tiles: qt0 .. qe-1 of each head, then the first plain tile
+      if (q.qt + 1 < qe) return Pos{q.g, q.qt + 1};
+      return q.g + 1 < G ? Pos{q.g + 1, qt0} : Pos{0, qe};
+    }
+    return q.qt + 1 < nqt ? Pos{q.g, q.qt + 1} : Pos{q.g + 1, qe};
+  };
   uint32_t qvoff[QPlan::NPW];
   dma_init<QPlan, kWaves, SWZ>(qvoff, row_bytes, wave, lane);
   // L and D of query row (tile start + tid), tid < BQ: loaded one tile before they are staged
@@ -158,33 +175,38 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
   // the load would make the wave wait there for the load and for the tile DMA issued just
   // before it (the counter is in order).
   float lraw = 0.f, draw = 0.f;
-  auto load_ld = [&](int qt) {
+  auto load_ld = [&](Pos ps) {
     if (tid < BQ) {
-      const int q = min(qt * BQ + tid, N - 1);   // in bounds; rows past the end are masked when staged
-      lraw = lse_h[q];
-      draw = del_h[q];
+      const size_t lh = ((size_t)b * H + kvh * G + ps.g) * N;
+      const int q = min(ps.qt * BQ + tid, N - 1);   // in bounds; rows past the end are masked when staged
+      lraw = p.lse[lh + q];
+      draw = p.delta[lh + q];
     }
   };
-  auto fetch_into = [&](int qt, char* st) {
+  auto fetch_into = [&](Pos ps, char* st) {
+    const int qt = ps.qt, hq = kvh * G + ps.g;
     if (tid < BQ) {
       const bool in = qt * BQ + tid < N;
       ((float*)(st + OFF_L))[tid] = in ? lraw * kLog2e : INFINITY;   // P = exp2(s*c - inf) = 0 past the end
       ((float*)(st + OFF_D))[tid] = in ? draw : 0.f;
     }
-    dma_issue<QPlan, kWaves>(qvoff, st, qbase, qt * BQ, row_bytes, nrec, wave);
-    dma_issue<QPlan, kWaves>(qvoff, st + OFF_DO, dobase, qt * BQ, row_bytes, nrec, wave);
+    const size_t qh_off = ((size_t)b * N * H + hq) * D * 2;
+    const uint32_t q_nrec = (uint32_t)N * row_bytes - (uint32_t)hq * D * 2;
+    dma_issue<QPlan, kWaves>(qvoff, st, (const char*)p.q + qh_off, qt * BQ, row_bytes, q_nrec, wave);
+    dma_issue<QPlan, kWaves>(qvoff, st + OFF_DO, (const char*)p.dout + qh_off, qt * BQ, row_bytes, q_nrec, wave);
   };
-  if (qt0 < nqt) {
-    load_ld(qt0);
-    fetch_into(qt0, smem);
-    if (qt0 + 1 < nqt) load_ld(qt0 + 1);
+  Pos pos0 = first_pos(), pos1 = next_pos(pos0), pos2 = next_pos(pos1);   // tiles u, u+1, u+2
+  if (NU > 0) {
+    load_ld(pos0);
+    fetch_into(pos0, smem);
+    if (1 < NU) load_ld(pos1);
   }
 
   u32x4 kreg[NKS], vreg[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    kreg[ks] = buf_load16(rk, (uint32_t)key * row_bytes + (16 * ks + 8 * hf) * 2);
-    vreg[ks] = buf_load16(rv, (uint32_t)key * row_bytes + (16 * ks + 8 * hf) * 2);
+    kreg[ks] = buf_load16(rk, (uint32_t)key * kv_row_bytes + (16 * ks + 8 * hf) * 2);
+    vreg[ks] = buf_load16(rv, (uint32_t)key * kv_row_bytes + (16 * ks + 8 * hf) * 2);
   }
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {   // waited for here, not inside the tile loop
@@ -344,33 +366,35 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
   // stages are distinct, and saying so (restrict) lets the compiler see that the tile's LDS
   // reads cannot alias the DMA in flight: otherwise it waits for that DMA before the first
   // transpose read of the tile.
-  auto body = [&](int qt, char* __restrict__ nxt, const char* __restrict__ cur, auto edge_tag) {
+  auto body = [&](int u, char* __restrict__ nxt, const char* __restrict__ cur, auto edge_tag) {
     constexpr bool EDGE = decltype(edge_tag)::value;
-    if (qt + 1 < nqt) {
-      fetch_into(qt + 1, nxt);
-      if (qt + 2 < nqt) load_ld(qt + 2);
+    if (u + 1 < NU) {
+      fetch_into(pos1, nxt);
+      if (u + 2 < NU) load_ld(pos2);
     }
-    const int q0 = qt * BQ;
+    const int q0 = pos0.qt * BQ;
     if constexpr (EDGE) {
       if (wave_live && q0 + BQ - 1 >= k0w) tile(cur, q0, std::true_type{});
     } else {
       tile(cur, q0, std::false_type{});
     }
   };
-  auto step = [&](int qt, auto edge_tag) {
+  auto step = [&](int u, auto edge_tag) {
     pin_all();
-    const int i = qt - qt0;
-    const int cur = __builtin_amdgcn_readfirstlane((i & 1) * STAGE);
-    body(qt, smem + (STAGE - cur), smem + cur, edge_tag);
+    const int cur = __builtin_amdgcn_readfirstlane((u & 1) * STAGE);
+    body(u, smem + (STAGE - cur), smem + cur, edge_tag);
+    pos0 = pos1;
+    pos1 = pos2;
+    pos2 = next_pos(pos2);
     wait_dma();
     __syncthreads();
     pin_all();
   };
-  int qt = qt0;
+  int u = 0;
   if constexpr (CAUSAL) {
-    for (; qt < nqt && qt * BQ < kt * BKV + BKV - 1; ++qt) step(qt, std::true_type{});
+    for (; u < UE; ++u) step(u, std::true_type{});
   }
-  for (; qt < nqt; ++qt) step(qt, std::false_type{});
+  for (; u < NU; ++u) step(u, std::false_type{});
 
   if (wave_live) {
     const float scale = p.scale;
@@ -383,8 +407,8 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
                           pack2<BF16>(dvacc[i][4 * rr + 2], dvacc[i][4 * rr + 3])};
         const u32x2 kk = {pack2<BF16>(dkacc[i][4 * rr + 0] * scale, dkacc[i][4 * rr + 1] * scale),
                           pack2<BF16>(dkacc[i][4 * rr + 2] * scale, dkacc[i][4 * rr + 3] * scale)};
-        buf_store8(rdv, (uint32_t)key * row_bytes + d0 * 2, vv);
-        buf_store8(rdk, (uint32_t)key * row_bytes + d0 * 2, kk);
+        buf_store8(rdv, (uint32_t)key * kv_row_bytes + d0 * 2, vv);
+        buf_store8(rdk, (uint32_t)key * kv_row_bytes + d0 * 2, kk);
       }
   }
 }
@@ -434,18 +458,23 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(BwdParams p)
   const auto rq = make_rsrc((const char*)p.q + head_off, nrec);
   const auto rdo = make_rsrc((const char*)p.dout + head_off, nrec);
   const auto rdq = make_rsrc((const char*)p.dq + head_off, nrec);
-  const char* kbase = (const char*)p.k + head_off;
-  const char* vbase = (const char*)p.v + head_off;
+  // K and V: [B][N][Hkv][D], key/value head h / (H / Hkv)
+  const int Hkv = p.Hkv, kvh = h / (H / Hkv);
+  const uint32_t kv_row_bytes = (uint32_t)Hkv * D * 2;
+  const size_t kv_head_off = ((size_t)b * N * Hkv + kvh) * D * 2;
+  const uint32_t kv_nrec = (uint32_t)N * kv_row_bytes - (uint32_t)kvh * D * 2;
+  const char* kbase = (const char*)p.k + kv_head_off;
+  const char* vbase = (const char*)p.v + kv_head_off;
 
   const int kend = CAUSAL ? min(N, (qt + 1) * BR) : N;
   const int nkt = (kend + BC - 1) / BC;
   const int nkt_w = q0 >= N ? 0 : CAUSAL ? min(nkt, (q0 + 31) / BC + 1) : nkt;
   uint32_t kvoff[KPlan::NPW], vvoff[VPlan::NPW];
-  dma_init<KPlan, kWaves, SWZ>(kvoff, row_bytes, wave, lane);
-  dma_init<VPlan, kWaves>(vvoff, row_bytes, wave, lane);
+  dma_init<KPlan, kWaves, SWZ>(kvoff, kv_row_bytes, wave, lane);
+  dma_init<VPlan, kWaves>(vvoff, kv_row_bytes, wave, lane);
   auto fetch_into = [&](int j, char* st) {
-    dma_issue<KPlan, kWaves>(kvoff, st, kbase, j * BC, row_bytes, nrec, wave);
-    dma_issue<VPlan, kWaves>(vvoff, st + KB, vbase, j * BC, row_bytes, nrec, wave);
+    dma_issue<KPlan, kWaves>(kvoff, st, kbase, j * BC, kv_row_bytes, kv_nrec, wave);
+    dma_issue<VPlan, kWaves>(vvoff, st + KB, vbase, j * BC, kv_row_bytes, kv_nrec, wave);
   };
   fetch_into(0, smem);
 
@@ -591,7 +620,7 @@ hipError_t launch_t(const BwdParams& p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nkvt = (p.N + kWaves * 32 - 1) / (kWaves * 32);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, CAUSAL>), dim3((unsigned)(p.B * p.H * nkvt)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, CAUSAL>), dim3((unsigned)(p.B * p.Hkv * nkvt)), dim3(256), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int nqt = (p.N + kWaves * 32 - 1) / (kWaves * 32);
   hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, CAUSAL>), dim3((unsigned)(p.B * p.H * nqt)), dim3(256), 0, s, p);

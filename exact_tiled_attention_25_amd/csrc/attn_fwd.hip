@@ -176,6 +176,11 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::WAVES, 1) void fwd_kernel(FwdParams
   const uint32_t nrec = (uint32_t)N * row_bytes - (uint32_t)h * D * 2;
   const auto rq = make_rsrc((const char*)p.q + head_off, nrec);
   const auto ro = make_rsrc((const char*)p.o + head_off, nrec);
+  // K and V: [B][N][Hkv][D], head h / (H / Hkv) (grouped key/value heads; Hkv = H is plain)
+  const int Hkv = p.Hkv, kvh = h / (H / Hkv);
+  const uint32_t kv_row_bytes = (uint32_t)Hkv * D * 2;
+  const size_t kv_head_off = ((size_t)b * N * Hkv + kvh) * D * 2;
+  const uint32_t kv_nrec = (uint32_t)N * kv_row_bytes - (uint32_t)kvh * D * 2;
 
   const int kend = CAUSAL ? min(N, (qt + 1) * kBR) : N;
   const int nkt_all = (kend + BC - 1) / BC;
@@ -199,12 +204,12 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::WAVES, 1) void fwd_kernel(FwdParams
   const int k_lane = k_lane_off<D>(lane), v_lane = v_lane_off<D>(lane);
   auto is_edge = [&](int j) { const int k0 = (t0 + j) * BC; return (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0); };
   uint32_t kvoff[KPlan::NPW], vvoff[VPlan::NPW];
-  dma_init<KPlan, kWaves>(kvoff, row_bytes, wave, lane);
-  dma_init<VPlan, kWaves>(vvoff, row_bytes, wave, lane);
-  const char* kbase = (const char*)p.k + head_off;
-  const char* vbase = (const char*)p.v + head_off;
-  auto dma_k = [&](int t) { dma_issue<KPlan, kWaves>(kvoff, kst(t), kbase, (t0 + t) * BC, row_bytes, nrec, wave); };
-  auto dma_v = [&](int t) { dma_issue<VPlan, kWaves>(vvoff, vst(t), vbase, (t0 + t) * BC, row_bytes, nrec, wave); };
+  dma_init<KPlan, kWaves>(kvoff, kv_row_bytes, wave, lane);
+  dma_init<VPlan, kWaves>(vvoff, kv_row_bytes, wave, lane);
+  const char* kbase = (const char*)p.k + kv_head_off;
+  const char* vbase = (const char*)p.v + kv_head_off;
+  auto dma_k = [&](int t) { dma_issue<KPlan, kWaves>(kvoff, kst(t), kbase, (t0 + t) * BC, kv_row_bytes, kv_nrec, wave); };
+  auto dma_v = [&](int t) { dma_issue<VPlan, kWaves>(vvoff, vst(t), vbase, (t0 + t) * BC, kv_row_bytes, kv_nrec, wave); };
 
   // Q^T operand: lane holds query q0 + l32, dims 16*ks + 8*hf .. +7.
   u32x4 qreg[NKS];

@@ -13,6 +13,7 @@ struct FwdParams {
   float* lse;
   int B, H, N;
   float c;  // softmax scale * log2(e): scores are exponentiated with exp2
+  int Hkv;  // key/value heads (divides H); query head h reads key/value head h / (H / Hkv)
   // split-KV only: S = splits part slots per query tile; a query tile with n key tiles
   // uses ceil(n / split_tiles) of them (split_tiles = ceil(ceil(N/64) / S)); the per-part
   // results O_s = O/l (fp32 [S][B][H][N][d]) and L_s (fp32 [S][B][H][N]; -inf: no keys of
@@ -37,6 +38,7 @@ struct BwdParams {
   int B, H, N;
   float scale;
   float c;  // scale * log2(e)
+  int Hkv;  // key/value heads (divides H); dK, dV are [B][N][Hkv][d]
 };
 
 struct Fp8QuantParams {

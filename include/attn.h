@@ -54,6 +54,15 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, flo
                        int B, int H, int N, int d, int causal, float scale,
                        attn_dtype_t dtype, attn_stream_t stream);
 
+/* Grouped-query forward: the key/value heads are shared by groups of query heads (the
+ * enterprise post, "Runtime Kernel Selection", lists grouped query attention among the
+ * supported patterns; it gives no formula). q, o: [B][N][H][d]; k, v: [B][N][H_kv][d] with
+ * 1 <= H_kv and H % H_kv == 0; query head h attends to key/value head h / (H / H_kv).
+ * Otherwise as attn_fwd (attn_fwd is the case H_kv = H). ATTN_EINVAL for a bad H_kv. */
+attn_status_t attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int H_kv, int N, int d, int causal, float scale,
+                           attn_dtype_t dtype, attn_stream_t stream);
+
 /* Bytes of device workspace attn_fwd_splitkv needs: per part, O_s fp32 [B][H][N][d] and
  * L_s fp32 [B][H][N] (num_splits * B*H*N*(d+1) * 4 bytes). 0 for invalid arguments. */
 size_t attn_fwd_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits);
@@ -87,6 +96,16 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
                        int B, int H, int N, int d, int causal, float scale,
                        attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
                        attn_stream_t stream);
+
+/* Grouped-query backward: shapes as attn_fwd_gqa; dq [B][N][H][d], dk and dv
+ * [B][N][H_kv][d]. A key/value head's dK and dV are the sums of the gradients through each of
+ * its H / H_kv query heads, formed in one workgroup per 128 keys (deterministic, no atomics).
+ * Workspace as attn_bwd (attn_bwd_workspace_bytes(B, H, N, d)); attn_bwd is H_kv = H. */
+attn_status_t attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           int B, int H, int H_kv, int N, int d, int causal, float scale,
+                           attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                           attn_stream_t stream);
 
 /* FP8 block quantisation ("FP8 accuracy controls": one fp32 scale per block; incoherent
  * processing multiplies Q and K by the same orthogonal M = diag(s) H_d / sqrt(d)).

@@ -60,6 +60,13 @@ def test_null_pointers_rejected(lib):
                         None, 0, None) == 1
     assert lib.attn_fp8_quantize(None, None, None, 1, 1, 16, 64, 0, 1, 0, None) == 1
     assert lib.attn_fp8_quantize_per_tensor(None, None, None, 1, 1, 16, 64, 0, 1, 0, None) == 1
+    assert lib.attn_fwd_gqa(None, None, None, None, None, 1, 4, 2, 16, 64, 0, 0.125, 0, None) == 1
+    assert lib.attn_fwd_gqa(None, None, None, None, None, 1, 4, 3, 16, 64, 0, 0.125, 0, None) == 1
+    assert lib.attn_fwd_gqa(None, None, None, None, None, 1, 4, 0, 16, 64, 0, 0.125, 0, None) == 1
+    assert lib.attn_bwd_gqa(None, None, None, None, None, None, None, None, None, 1, 4, 2, 16, 64, 0, 0.125, 0,
+                            None, 0, None) == 1
+    assert lib.attn_bwd_gqa(None, None, None, None, None, None, None, None, None, 1, 6, 4, 16, 64, 0, 0.125, 0,
+                            None, 0, None) == 1
     assert lib.attn_fwd_splitkv(None, None, None, None, None, 1, 1, 16, 64, 0, 0.125, 0, 2, None, 0, None) == 1
     assert lib.attn_fwd_splitkv(None, None, None, None, None, 1, 1, 16, 64, 0, 0.125, 0, 0, None, 0, None) == 1
     assert lib.attn_fwd_splitkv(None, None, None, None, None, 1, 1, 16, 96, 0, 0.125, 0, 2, None, 0, None) == 2
