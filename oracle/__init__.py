@@ -17,7 +17,8 @@ Pin status of every function is stated in its module docstring; every function h
 pinned by a ``-m "not gpu"`` test in ``tests/test_oracle_*.py``.
 """
 from .attention import (forward, forward_rows, backward, head_forward, head_backward,  # noqa: F401
-                        head_probs, flops_forward, kv_head)
+                        head_probs, flops_forward, kv_head, forward_varlen,
+                        backward_varlen)
 from .fp8 import (e4m3_decode, e4m3_encode, e4m3_finite_values, splitmix64, hadamard_signs,  # noqa: F401
                   sylvester_hadamard, rotation_matrix, quantize_blocks, quantize_per_tensor,
                   dequantize_blocks,

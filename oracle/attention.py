@@ -15,6 +15,10 @@ Readings where the pages are silent:
   * log base of L: natural log, as written in the Symbol Map.
   * causal mask: key j is visible to query i iff j <= i (equal query and key lengths).
   * layout: tensors are [B, N, H, d] (token-major); L is [B, H, N].
+  * variable-length batches (the enterprise post, "GPU Compatibility and Enablement Matrix",
+    names variable-length sequence handling as a coming feature): sequences packed back to
+    back, [T, heads, d], delimited by offsets cu_seqlens; each is an independent attention and
+    L is [H, T].
   * grouped-query attention: the enterprise post ("FlashAttention 3 Hardware Acceleration",
     section "Runtime Kernel Selection") names the pattern without a formula. Reading: K and V
     may have Hkv heads, Hkv dividing H; query head h reads key/value head h // (H / Hkv); a
@@ -28,7 +32,9 @@ scipy's logsumexp/softmax, central finite differences, invariants (rows of P sum
 constant V, key permutation, sum of dK = 0, sum of dV = sum of dO), closed forms (one-hot
 scores, scale = 0, N = 1, causal row 0) and the split-KV log-sum-exp merge identity; for
 grouped key/value heads, torch's fp64 grouped-query attention and its autograd, and central
-finite differences through a shared head.
+finite differences through a shared head; for packed variable-length batches, isolation of
+each sequence from the others' contents, and per-sequence closed forms (scale = 0 prefix
+means, causal first rows).
 """
 import numpy as np
 
@@ -158,6 +164,40 @@ def backward(q, k, v, do, causal=False, scale=None):
             dq[b, :, h] = dqh
             dk[b, :, g] += dkh
             dv[b, :, g] += dvh
+    return dq, dk, dv
+
+
+def _spans(cu_seqlens):
+    cu = [int(x) for x in np.asarray(cu_seqlens).reshape(-1)]
+    if cu[0] != 0 or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must start at 0 and not decrease")
+    return list(zip(cu[:-1], cu[1:]))
+
+
+def forward_varlen(q, k, v, cu_seqlens, causal=False, scale=None):
+    """Packed variable-length batch: q [T, H, d], k and v [T, Hkv, d]; sequence b is rows
+    cu_seqlens[b] .. cu_seqlens[b+1]-1 and is an independent attention (the causal mask is
+    within the sequence). Returns O [T, H, d] and L [H, T] in fp64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, H, d = q.shape
+    o = np.zeros((T, H, v.shape[2]))
+    lse = np.zeros((H, T))
+    for s0, s1 in _spans(cu_seqlens):
+        if s1 > s0:
+            ob, lb = forward(q[None, s0:s1], k[None, s0:s1], v[None, s0:s1], causal, scale)
+            o[s0:s1], lse[:, s0:s1] = ob[0], lb[0]
+    return o, lse
+
+
+def backward_varlen(q, k, v, do, cu_seqlens, causal=False, scale=None):
+    """Gradients of sum(dO o O) for a packed variable-length batch (shapes as in
+    forward_varlen); returns fp64 (dQ, dK, dV)."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for s0, s1 in _spans(cu_seqlens):
+        if s1 > s0:
+            g = backward(q[None, s0:s1], k[None, s0:s1], v[None, s0:s1], do[None, s0:s1], causal, scale)
+            dq[s0:s1], dk[s0:s1], dv[s0:s1] = (x[0] for x in g)
     return dq, dk, dv
 
 

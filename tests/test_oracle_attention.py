@@ -251,6 +251,60 @@ def test_grouped_kv_heads_finite_differences():
             assert np.abs(fd - grad).max() <= 1e-6 * np.abs(grad).max(), (causal, which)
 
 
+CU = [0, 5, 5, 17, 18, 40]   # lengths 5, 0, 12, 1, 22
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_sequences_are_isolated(causal):
+    """Changing every other sequence's Q, K, V and dO leaves a sequence's O, L and gradients
+    unchanged, and gradients never leak into another sequence's rows."""
+    T, H, hkv, d = CU[-1], 4, 2, 8
+    q, do = _rand(T, H, d), _rand(T, H, d)
+    k, v = _rand(T, hkv, d), _rand(T, hkv, d)
+    o, lse = oracle.forward_varlen(q, k, v, CU, causal, 0.6)
+    g = oracle.backward_varlen(q, k, v, do, CU, causal, 0.6)
+    s0, s1 = 5, 17
+    outside = np.r_[0:s0, s1:T]
+    q2, k2, v2, do2 = (x.copy() for x in (q, k, v, do))
+    for x in (q2, k2, v2, do2):
+        x[outside] = _rand(len(outside), *x.shape[1:])
+    o2, lse2 = oracle.forward_varlen(q2, k2, v2, CU, causal, 0.6)
+    g2 = oracle.backward_varlen(q2, k2, v2, do2, CU, causal, 0.6)
+    np.testing.assert_array_equal(o[s0:s1], o2[s0:s1])
+    np.testing.assert_array_equal(lse[:, s0:s1], lse2[:, s0:s1])
+    for a, b in zip(g, g2):
+        np.testing.assert_array_equal(a[s0:s1], b[s0:s1])
+    # dO zero outside the sequence: no gradient anywhere outside it
+    do3 = np.zeros_like(do)
+    do3[s0:s1] = do[s0:s1]
+    for x in oracle.backward_varlen(q, k, v, do3, CU, causal, 0.6):
+        assert np.abs(x[outside]).max() == 0.0
+
+
+def test_varlen_closed_forms():
+    """scale = 0: each sequence's O is the (prefix) mean of its own V and L = log of the
+    number of visible keys; causal: the first row of each sequence is its first V row."""
+    T, H, d = CU[-1], 2, 4
+    q, k, v = _rand(T, H, d), _rand(T, H, d), _rand(T, H, d)
+    for causal in (False, True):
+        o, lse = oracle.forward_varlen(q, k, v, CU, causal, 0.0)
+        for s0, s1 in zip(CU[:-1], CU[1:]):
+            if s1 == s0:
+                continue
+            n = np.arange(1, s1 - s0 + 1)
+            if causal:
+                ref = np.cumsum(v[s0:s1], axis=0) / n[:, None, None]
+                np.testing.assert_allclose(lse[:, s0:s1], np.broadcast_to(np.log(n), (H, s1 - s0)), atol=1e-14)
+            else:
+                ref = np.broadcast_to(v[s0:s1].mean(axis=0), v[s0:s1].shape)
+                np.testing.assert_allclose(lse[:, s0:s1], np.log(s1 - s0), atol=1e-14)
+            np.testing.assert_allclose(o[s0:s1], ref, atol=1e-14)
+        oc, _ = oracle.forward_varlen(q, k, v, CU, True, 0.9)
+        for s0, s1 in zip(CU[:-1], CU[1:]):
+            if s1 > s0:
+                np.testing.assert_allclose(oc[s0], v[s0], atol=1e-14)
+
+
 def test_kv_head_mapping():
     assert [oracle.kv_head(h, 8, 2) for h in range(8)] == [0, 0, 0, 0, 1, 1, 1, 1]
     assert [oracle.kv_head(h, 4, 4) for h in range(4)] == [0, 1, 2, 3]

@@ -69,8 +69,14 @@ def _kv_head_interleaved(h, H, Hkv):
     return h % Hkv
 
 
+def _varlen_as_one_sequence(q, k, v, cu_seqlens, causal=False, scale=None):
+    o, lse = A.forward(A._f64(q)[None], A._f64(k)[None], A._f64(v)[None], causal, scale)
+    return o[0], lse[0]
+
+
 ATTN_CASES = {
     "grouped heads interleaved": ("kv_head", _kv_head_interleaved),
+    "packed sequences attend across": ("forward_varlen", _varlen_as_one_sequence),
     "flipped causal mask": ("_scores", _scores_flipped_mask),
     "dropped scale": ("_scores", _scores_no_scale),
     "log2 lse": ("head_forward", _fwd_log2),
@@ -89,6 +95,8 @@ def _attention_pins():
         (TA.test_backward_matches_torch_autograd, (2, 5, 2, 8), False),
         (TA.test_backward_finite_differences, 8, 8, True),
         (TA.test_grouped_kv_heads_match_torch, 2, True),
+        (TA.test_varlen_sequences_are_isolated, True),
+        (TA.test_varlen_closed_forms,),
     ]
 
 
@@ -96,6 +104,7 @@ def _attention_pins():
 def test_attention_mutation_is_caught(monkeypatch, name):
     attr, bad = ATTN_CASES[name]
     monkeypatch.setattr(A, attr, bad)
+    monkeypatch.setattr(oracle, attr, bad, raising=False)
     assert any(_fails(fn, *args) for fn, *args in _attention_pins()), name
 
 

@@ -58,6 +58,30 @@ def make_inputs(B, N, H, d, dtype="bf16", seed=0, input_scale=1.0, outlier_frac=
     return out
 
 
+def ragged_lengths(B, mean, seed, min_len=0):
+    """B sequence lengths drawn uniformly from [min_len, 2*mean] (seeded): a mixed-length batch."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    return torch.randint(min_len, 2 * mean + 1, (B,), generator=g).tolist()
+
+
+def make_varlen_inputs(lengths, H, H_kv, d, dtype="bf16", seed=0, with_do=False, pad_rows=0, device="cpu"):
+    """Packed variable-length batch: sequences of the given lengths stacked along the token axis
+    (plus `pad_rows` trailing rows that belong to no sequence). Returns dict(q [T, H, d],
+    k, v [T, H_kv, d][, do [T, H, d]], cu_seqlens int32 [B+1], max_seqlen), drawn in the order
+    Q, K, V, dO as standard normals and cast to the dtype."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    cu = [0]
+    for n in lengths:
+        cu.append(cu[-1] + int(n))
+    T = cu[-1] + pad_rows
+    out = {}
+    for name, heads in (("q", H), ("k", H_kv), ("v", H_kv)) + ((("do", H),) if with_do else ()):
+        out[name] = torch.randn((T, heads, d), generator=g, dtype=torch.float32).to(DTYPES[dtype]).to(device)
+    out["cu_seqlens"] = torch.tensor(cu, dtype=torch.int32, device=device)
+    out["max_seqlen"] = max([int(n) for n in lengths], default=0)
+    return out
+
+
 def config_inputs(name, with_do=None, device="cpu", seed=None):
     c = CONFIGS[name]
     return make_inputs(c["B"], c["N"], c["H"], c["d"], c["dtype"], c["seed"] if seed is None else seed,
