@@ -283,7 +283,8 @@ def test_varlen_sequences_are_isolated(causal):
 
 def test_varlen_closed_forms():
     """scale = 0: each sequence's O is the (prefix) mean of its own V and L = log of the
-    number of visible keys; causal: the first row of each sequence is its first V row."""
+    number of visible keys; causal: the first row of each sequence is its first V row; a
+    one-token sequence has O = v and L = scale * q.k."""
     T, H, d = CU[-1], 2, 4
     q, k, v = _rand(T, H, d), _rand(T, H, d), _rand(T, H, d)
     for causal in (False, True):
@@ -299,10 +300,12 @@ def test_varlen_closed_forms():
                 ref = np.broadcast_to(v[s0:s1].mean(axis=0), v[s0:s1].shape)
                 np.testing.assert_allclose(lse[:, s0:s1], np.log(s1 - s0), atol=1e-14)
             np.testing.assert_allclose(o[s0:s1], ref, atol=1e-14)
-        oc, _ = oracle.forward_varlen(q, k, v, CU, True, 0.9)
+        oc, lc = oracle.forward_varlen(q, k, v, CU, causal, 0.9)
         for s0, s1 in zip(CU[:-1], CU[1:]):
-            if s1 > s0:
+            if s1 > s0 and (causal or s1 == s0 + 1):
                 np.testing.assert_allclose(oc[s0], v[s0], atol=1e-14)
+        # the one-token sequence (row 17): O = v and L = scale * q.k, per head
+        np.testing.assert_allclose(lc[:, 17], 0.9 * np.einsum("hd,hd->h", q[17], k[17]), atol=1e-14)
 
 
 def test_kv_head_mapping():
