@@ -19,8 +19,9 @@ LIB_PATH = os.path.join(_HERE, "libattn.so")
 
 ATTN_BF16, ATTN_FP16 = 0, 1
 FP8_BLOCK = 64
-EXPORTS = ("attn_fwd", "attn_fwd_gqa", "attn_fwd_splitkv_workspace_bytes", "attn_fwd_splitkv",
-           "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_gqa", "attn_fp8_quantize",
+EXPORTS = ("attn_fwd", "attn_fwd_gqa", "attn_fwd_varlen", "attn_fwd_splitkv_workspace_bytes",
+           "attn_fwd_splitkv", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_gqa",
+           "attn_bwd_varlen_workspace_bytes", "attn_bwd_varlen", "attn_fp8_quantize",
            "attn_fp8_quantize_per_tensor", "attn_fwd_fp8", "attn_strerror")
 _DTYPE_CODE = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_FP16}
 
@@ -47,6 +48,12 @@ def load(path=None):
     L.attn_fwd.restype = i
     L.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     L.attn_fwd_gqa.restype = i
+    L.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    L.attn_fwd_varlen.restype = i
+    L.attn_bwd_varlen_workspace_bytes.argtypes = [i, i]
+    L.attn_bwd_varlen_workspace_bytes.restype = sz
+    L.attn_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp, sz, vp]
+    L.attn_bwd_varlen.restype = i
     L.attn_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
     L.attn_fwd_splitkv_workspace_bytes.restype = sz
     L.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
@@ -160,6 +167,59 @@ def attn_bwd_gqa(q, k, v, o, lse, do, causal=False, scale=None, dq=None, dk=None
     _check("attn_bwd_gqa", load().attn_bwd_gqa(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), B, H, hkv, N, d,
         int(bool(causal)), _default_scale(d, scale), _DTYPE_CODE[q.dtype], _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q, stream)))
+    return dq, dk, dv
+
+
+def _varlen_args(q, k, cu_seqlens, max_seqlen):
+    _tensor(q, "q", dtypes=tuple(_DTYPE_CODE))
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, d] (packed sequences)")
+    T, H, d = q.shape
+    _tensor(k, "k", dtypes=(q.dtype,), device=q.device)
+    hkv = k.shape[1] if k.dim() == 3 else 0
+    _tensor(k, "k", (T, hkv, d), (q.dtype,), q.device)
+    _tensor(cu_seqlens, "cu_seqlens", dtypes=(torch.int32,), device=q.device)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor of B+1 offsets")
+    return T, H, hkv, d, cu_seqlens.numel() - 1, int(max_seqlen)
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, o=None, lse=None, stream=None):
+    """Packed variable-length forward: q [T, H, d], k, v [T, H_kv, d], cu_seqlens int32 [B+1]
+    on the device, max_seqlen >= every length. Returns O [T, H, d] and LSE [H, T] fp32."""
+    T, H, hkv, d, B, ms = _varlen_args(q, k, cu_seqlens, max_seqlen)
+    _tensor(v, "v", tuple(k.shape), (q.dtype,), q.device)
+    o = torch.empty_like(q) if o is None else _tensor(o, "o", q.shape, (q.dtype,), q.device)
+    lse = (torch.empty((H, T), dtype=torch.float32, device=q.device) if lse is None
+           else _tensor(lse, "lse", (H, T), (torch.float32,), q.device))
+    _check("attn_fwd_varlen", load().attn_fwd_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens), B, T, ms, H, hkv, d, int(bool(causal)),
+        _default_scale(d, scale), _DTYPE_CODE[q.dtype], _stream(q, stream)))
+    return o, lse
+
+
+def attn_bwd_varlen_workspace_bytes(T, H):
+    return int(load().attn_bwd_varlen_workspace_bytes(T, H))
+
+
+def attn_bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, causal=False, scale=None, dq=None, dk=None,
+                    dv=None, workspace=None, stream=None):
+    """Backward of attn_fwd_varlen (layouts as there)."""
+    T, H, hkv, d, B, ms = _varlen_args(q, k, cu_seqlens, max_seqlen)
+    _tensor(v, "v", tuple(k.shape), (q.dtype,), q.device)
+    for name, t in (("o", o), ("do", do)):
+        _tensor(t, name, q.shape, (q.dtype,), q.device)
+    _tensor(lse, "lse", (H, T), (torch.float32,), q.device)
+    dq = torch.empty_like(q) if dq is None else _tensor(dq, "dq", q.shape, (q.dtype,), q.device)
+    dk = torch.empty_like(k) if dk is None else _tensor(dk, "dk", tuple(k.shape), (q.dtype,), q.device)
+    dv = torch.empty_like(v) if dv is None else _tensor(dv, "dv", tuple(k.shape), (q.dtype,), q.device)
+    if workspace is None:
+        workspace = torch.empty(max(attn_bwd_varlen_workspace_bytes(T, H), 1), dtype=torch.uint8, device=q.device)
+    _tensor(workspace, "workspace", device=q.device)
+    _check("attn_bwd_varlen", load().attn_bwd_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens), B, T,
+        ms, H, hkv, d, int(bool(causal)), _default_scale(d, scale), _DTYPE_CODE[q.dtype], _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(q, stream)))
     return dq, dk, dv
 

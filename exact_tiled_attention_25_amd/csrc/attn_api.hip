@@ -60,9 +60,11 @@ uint64_t splitmix64_output(uint64_t seed, uint64_t t) {
 
 extern "C" {
 
+// Variable-length batches: cu (device, B+1 offsets) and T (total tokens); otherwise null, 0.
 static attn_status_t fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int B, int H, int Hkv, int N, int d, int causal, float scale,
-                                attn_dtype_t dtype, attn_stream_t stream) {
+                                attn_dtype_t dtype, attn_stream_t stream, const int* cu = nullptr,
+                                int T = 0) {
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_EINVAL;
   if (bad_scale(scale)) return ATTN_EINVAL;
   bool empty = false;
@@ -72,7 +74,7 @@ static attn_status_t fwd_common(const void* q, const void* k, const void* v, voi
   if (empty) return ATTN_OK;
   if (!q || !k || !v || !o || !lse) return ATTN_EINVAL;
   if ((st = check_device()) != ATTN_OK) return st;
-  attn::FwdParams p{q, k, v, o, lse, B, H, N, (float)(scale * kLog2e), Hkv};
+  attn::FwdParams p{q, k, v, o, lse, B, H, N, (float)(scale * kLog2e), Hkv, cu, T};
   (void)hipGetLastError();
   return launched(attn::launch_fwd(dtype == ATTN_BF16, d, causal != 0, p, (hipStream_t)stream));
 }
@@ -87,6 +89,28 @@ attn_status_t attn_fwd_gqa(const void* q, const void* k, const void* v, void* o,
                            int B, int H, int H_kv, int N, int d, int causal, float scale,
                            attn_dtype_t dtype, attn_stream_t stream) {
   return fwd_common(q, k, v, o, lse, B, H, H_kv, N, d, causal, scale, dtype, stream);
+}
+
+// Checks of a variable-length batch that need no device access (the offsets live there).
+static attn_status_t check_varlen(const int* cu, int B, int T, int max_seqlen, int H, bool* empty) {
+  if (B < 0 || T < 0 || max_seqlen < 0 || H < 0) return ATTN_EINVAL;
+  if (B > 0 && T > 0 && max_seqlen > 0 && H > 0 && !cu) return ATTN_EINVAL;
+  if ((double)T * H * 4 >= 2147483647.0 * 8) return ATTN_EUNSUPPORTED;   // per-row kernels' grids
+  *empty = B == 0 || T == 0 || max_seqlen == 0 || H == 0;
+  return ATTN_OK;
+}
+
+attn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const int* cu_seqlens, int B, int T, int max_seqlen, int H, int H_kv,
+                              int d, int causal, float scale, attn_dtype_t dtype,
+                              attn_stream_t stream) {
+  bool empty = false;
+  attn_status_t st = check_varlen(cu_seqlens, B, T, max_seqlen, H, &empty);
+  if (st != ATTN_OK) return st;
+  if (!supported_d(d)) return ATTN_EUNSUPPORTED;
+  if (empty) return (H_kv < 1 || (H > 0 && H % H_kv != 0)) ? ATTN_EINVAL : ATTN_OK;
+  return fwd_common(q, k, v, o, lse, B, H, H_kv, max_seqlen, d, causal, scale, dtype, stream,
+                    cu_seqlens, T);
 }
 
 size_t attn_fwd_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits) {
@@ -112,7 +136,7 @@ attn_status_t attn_fwd_splitkv(const void* q, const void* k, const void* v, void
     return ATTN_EWORKSPACE;
   if ((st = check_device()) != ATTN_OK) return st;
   float* ws = (float*)workspace;
-  attn::FwdParams p{q, k, v, o, lse, B, H, N, (float)(scale * kLog2e), H, num_splits, ws,
+  attn::FwdParams p{q, k, v, o, lse, B, H, N, (float)(scale * kLog2e), H, nullptr, 0, num_splits, ws,
                     ws + (size_t)num_splits * B * H * N * d};
   (void)hipGetLastError();
   return launched(attn::launch_fwd_splitkv(dtype == ATTN_BF16, d, causal != 0, p, (hipStream_t)stream));
@@ -128,7 +152,7 @@ static attn_status_t bwd_common(const void* q, const void* k, const void* v, con
                                 const float* lse, const void* dout, void* dq, void* dk, void* dv,
                                 int B, int H, int Hkv, int N, int d, int causal, float scale,
                                 attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
-                                attn_stream_t stream) {
+                                attn_stream_t stream, const int* cu = nullptr, int T = 0) {
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_EINVAL;
   if (bad_scale(scale)) return ATTN_EINVAL;
   bool empty = false;
@@ -137,10 +161,11 @@ static attn_status_t bwd_common(const void* q, const void* k, const void* v, con
   if (Hkv < 1 || (H > 0 && H % Hkv != 0)) return ATTN_EINVAL;
   if (empty) return ATTN_OK;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_EINVAL;
-  if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, H, N, d)) return ATTN_EWORKSPACE;
+  const size_t need = cu ? attn_bwd_varlen_workspace_bytes(T, H) : attn_bwd_workspace_bytes(B, H, N, d);
+  if (!workspace || workspace_bytes < need) return ATTN_EWORKSPACE;
   if ((st = check_device()) != ATTN_OK) return st;
   attn::BwdParams p{q, k, v, o, lse, dout, dq, dk, dv, (float*)workspace, B, H, N, scale,
-                    (float)(scale * kLog2e), Hkv};
+                    (float)(scale * kLog2e), Hkv, cu, T};
   (void)hipGetLastError();
   return launched(attn::launch_bwd(dtype == ATTN_BF16, d, causal != 0, p, (hipStream_t)stream));
 }
@@ -152,6 +177,25 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
                        attn_stream_t stream) {
   return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, B, H, H > 0 ? H : 1, N, d, causal, scale, dtype,
                     workspace, workspace_bytes, stream);
+}
+
+size_t attn_bwd_varlen_workspace_bytes(int T, int H) {
+  if (T <= 0 || H <= 0) return 0;
+  return (size_t)T * H * sizeof(float);
+}
+
+attn_status_t attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                              const int* cu_seqlens, int B, int T, int max_seqlen, int H, int H_kv,
+                              int d, int causal, float scale, attn_dtype_t dtype, void* workspace,
+                              size_t workspace_bytes, attn_stream_t stream) {
+  bool empty = false;
+  attn_status_t st = check_varlen(cu_seqlens, B, T, max_seqlen, H, &empty);
+  if (st != ATTN_OK) return st;
+  if (!supported_d(d)) return ATTN_EUNSUPPORTED;
+  if (empty) return (H_kv < 1 || (H > 0 && H % H_kv != 0)) ? ATTN_EINVAL : ATTN_OK;
+  return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, max_seqlen, d, causal, scale, dtype,
+                    workspace, workspace_bytes, stream, cu_seqlens, T);
 }
 
 attn_status_t attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o,

@@ -51,8 +51,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   constexpr int TPR = D / 8;       // threads per (token, head) row, 16 bytes each
   constexpr int RPB = 256 / TPR;   // rows per workgroup
   const int tid = threadIdx.x;
-  const long nrows = (long)p.B * p.N * p.H;
-  const long row = (long)blockIdx.x * RPB + tid / TPR;   // row = (b*N + n)*H + h
+  // rows (token, head): (b*N + n)*H + h, or t*H + h of the packed variable-length tokens
+  const long nrows = p.cu ? (long)p.T * p.H : (long)p.B * p.N * p.H;
+  const long row = (long)blockIdx.x * RPB + tid / TPR;
   float acc = 0.f;
   if (row < nrows) {
     const u32x4 a = *(const u32x4*)((const char*)p.o + row * (D * 2) + (tid % TPR) * 16);
@@ -71,8 +72,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   if (row < nrows && tid % TPR == 0) {
     const int h = (int)(row % p.H);
     const long bn = row / p.H;
-    const int n = (int)(bn % p.N), b = (int)(bn / p.N);
-    p.delta[((long)b * p.H + h) * p.N + n] = acc;
+    if (p.cu) {
+      p.delta[(long)h * p.T + bn] = acc;
+    } else {
+      const int n = (int)(bn % p.N), b = (int)(bn / p.N);
+      p.delta[((long)b * p.H + h) * p.N + n] = acc;
+    }
   }
 }
 
@@ -130,18 +135,21 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps loop control scalar
   const int l32 = lane & 31, hf = lane >> 5;
-  const int H = p.H, N = p.N, Hkv = p.Hkv, G = H / Hkv;
-  const int nkvt = (N + BKV - 1) / BKV;
+  const int H = p.H, Hkv = p.Hkv, G = H / Hkv;
+  const int nkvt = (p.N + BKV - 1) / BKV;   // p.N: the (longest) sequence length
   const int work = xcd_remap(blockIdx.x, gridDim.x);
   const int kt = work % nkvt;          // causal: low key tiles see the most queries; they go first
-  const int bh = work / nkvt;
+  const int bh = spread_pair(work / nkvt, p.B * Hkv, p.cu != nullptr);
   const int kvh = bh % Hkv, b = bh / Hkv;   // key/value head; its query heads are kvh*G .. +G-1
+  const SeqView sv = seq_view(p.cu, b, p.N, p.T);
+  const int N = sv.len;
+  if (kt * BKV >= N) return;   // a shorter sequence of a variable-length batch: nothing here
   const int k0w = kt * BKV + wave * 32;
   const int key = k0w + l32;
 
   // K, V, dK, dV: [B][N][Hkv][D]; Q, dO: [B][N][H][D]; L, D: [B][H][N]
   const uint32_t kv_row_bytes = (uint32_t)Hkv * D * 2;
-  const size_t kv_head_off = ((size_t)b * N * Hkv + kvh) * D * 2;
+  const size_t kv_head_off = ((size_t)sv.start * Hkv + kvh) * D * 2;
   const uint32_t kv_nrec = (uint32_t)N * kv_row_bytes - (uint32_t)kvh * D * 2;
   const auto rk = make_rsrc((const char*)p.k + kv_head_off, kv_nrec);
   const auto rv = make_rsrc((const char*)p.v + kv_head_off, kv_nrec);
@@ -177,7 +185,7 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
   float lraw = 0.f, draw = 0.f;
   auto load_ld = [&](Pos ps) {
     if (tid < BQ) {
-      const size_t lh = ((size_t)b * H + kvh * G + ps.g) * N;
+      const size_t lh = stat_row(p.cu, p.T, b, H, kvh * G + ps.g, sv);
       const int q = min(ps.qt * BQ + tid, N - 1);   // in bounds; rows past the end are masked when staged
       lraw = p.lse[lh + q];
       draw = p.delta[lh + q];
@@ -190,7 +198,7 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
       ((float*)(st + OFF_L))[tid] = in ? lraw * kLog2e : INFINITY;   // P = exp2(s*c - inf) = 0 past the end
       ((float*)(st + OFF_D))[tid] = in ? draw : 0.f;
     }
-    const size_t qh_off = ((size_t)b * N * H + hq) * D * 2;
+    const size_t qh_off = ((size_t)sv.start * H + hq) * D * 2;
     const uint32_t q_nrec = (uint32_t)N * row_bytes - (uint32_t)hq * D * 2;
     dma_issue<QPlan, kWaves>(qvoff, st, (const char*)p.q + qh_off, qt * BQ, row_bytes, q_nrec, wave);
     dma_issue<QPlan, kWaves>(qvoff, st + OFF_DO, (const char*)p.dout + qh_off, qt * BQ, row_bytes, q_nrec, wave);
@@ -442,18 +450,21 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(BwdParams p)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
-  const int H = p.H, N = p.N;
-  const int nqt = (N + BR - 1) / BR;
+  const int H = p.H;
+  const int nqt = (p.N + BR - 1) / BR;   // p.N: the (longest) sequence length
   const int work = xcd_remap(blockIdx.x, gridDim.x);
   const int qi = work % nqt;
-  const int bh = work / nqt;
+  const int bh = spread_pair(work / nqt, p.B * H, p.cu != nullptr);
   const int h = bh % H, b = bh / H;
+  const SeqView sv = seq_view(p.cu, b, p.N, p.T);
+  const int N = sv.len;
   const int qt = CAUSAL ? nqt - 1 - qi : qi;
+  if (qt * BR >= N) return;   // a shorter sequence of a variable-length batch: nothing here
   const int q0 = qt * BR + wave * 32;
   const int qrow = q0 + l32;
 
   const uint32_t row_bytes = (uint32_t)H * D * 2;
-  const size_t head_off = ((size_t)b * N * H + h) * D * 2;
+  const size_t head_off = ((size_t)sv.start * H + h) * D * 2;
   const uint32_t nrec = (uint32_t)N * row_bytes - (uint32_t)h * D * 2;
   const auto rq = make_rsrc((const char*)p.q + head_off, nrec);
   const auto rdo = make_rsrc((const char*)p.dout + head_off, nrec);
@@ -461,7 +472,7 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(BwdParams p)
   // K and V: [B][N][Hkv][D], key/value head h / (H / Hkv)
   const int Hkv = p.Hkv, kvh = h / (H / Hkv);
   const uint32_t kv_row_bytes = (uint32_t)Hkv * D * 2;
-  const size_t kv_head_off = ((size_t)b * N * Hkv + kvh) * D * 2;
+  const size_t kv_head_off = ((size_t)sv.start * Hkv + kvh) * D * 2;
   const uint32_t kv_nrec = (uint32_t)N * kv_row_bytes - (uint32_t)kvh * D * 2;
   const char* kbase = (const char*)p.k + kv_head_off;
   const char* vbase = (const char*)p.v + kv_head_off;
@@ -485,8 +496,9 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(BwdParams p)
     doreg[ks] = buf_load16(rdo, (uint32_t)qrow * row_bytes + (16 * ks + 8 * hf) * 2);
   }
   const bool row_ok = qrow < N;
-  const float lse2 = row_ok ? p.lse[((size_t)b * H + h) * N + qrow] * kLog2e : 0.f;
-  const float drow = row_ok ? p.delta[((size_t)b * H + h) * N + qrow] : 0.f;
+  const size_t stat_i = stat_row(p.cu, p.T, b, H, h, sv) + qrow;
+  const float lse2 = row_ok ? p.lse[stat_i] * kLog2e : 0.f;
+  const float drow = row_ok ? p.delta[stat_i] : 0.f;
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {   // waited for here, not inside the tile loop
     settle(qreg[ks]);
@@ -614,7 +626,7 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(BwdParams p)
 
 template <bool BF16, int D, bool CAUSAL>
 hipError_t launch_t(const BwdParams& p, hipStream_t s) {
-  const long nrows = (long)p.B * p.N * p.H;
+  const long nrows = p.cu ? (long)p.T * p.H : (long)p.B * p.N * p.H;
   const int rpb = 256 / (D / 8);
   hipLaunchKernelGGL((bwd_pre_kernel<BF16, D>), dim3((unsigned)((nrows + rpb - 1) / rpb)), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();

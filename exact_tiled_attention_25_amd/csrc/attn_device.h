@@ -93,6 +93,21 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblk) {
   return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
+// Inverse of xcd_remap: the block index that xcd_remap sends to v (0 <= v < n).
+__device__ __forceinline__ int xcd_unremap(int v, int n) {
+  const int q = n >> 3, r = n & 7;
+  const int x = v < r * (q + 1) ? v / (q + 1) : r + (v - r * (q + 1)) / max(q, 1);
+  return (v - x * q - min(x, r)) * 8 + x;
+}
+// (sequence, head) pair of virtual pair index vp. Fixed lengths: vp itself, so the XCD that
+// owns a contiguous range of work items runs a few whole heads. Variable lengths: the pairs
+// are dealt to the XCDs round-robin (pair p to the XCD range of class p % 8, with the tiles
+// of one pair kept together for L2 reuse of its K and V), so that every XCD holds a share of
+// every sequence instead of whole sequences of very different lengths.
+__device__ __forceinline__ int spread_pair(int vp, int npairs, bool varlen) {
+  return varlen ? xcd_unremap(vp, npairs) : vp;
+}
+
 // Compile-time loop: f(std::integral_constant<int, I>{}) for I = 0 .. N-1, fully expanded
 // (unlike #pragma unroll, which gives up on large bodies and leaves register arrays
 // dynamically indexed).
@@ -124,6 +139,25 @@ __device__ __forceinline__ void pin_acc(f32x16& x) { asm volatile("" : "+a"(x));
 __device__ __forceinline__ void pin_acc(u32x4& x) { asm volatile("" : "+a"(x)); }
 // An MFMA result that the VALU consumes next stays in VGPRs.
 __device__ __forceinline__ void pin_vgpr(f32x16& x) { asm volatile("" : "+v"(x)); }
+
+// Sequence b of a batch: its first token row and its length. Fixed-length batches (cu =
+// null): b * N and N. Variable-length batches: cu_seqlens[b] and cu_seqlens[b+1] - that.
+struct SeqView {
+  int start, len;
+};
+// The offsets are clamped to [0, T] and the length to N (the longest sequence), so that
+// malformed offsets give unspecified results but never an access outside the tensors.
+__device__ __forceinline__ SeqView seq_view(const int* cu, int b, int N, int T) {
+  if (cu == nullptr) return SeqView{b * N, N};
+  const int s0 = min(max(cu[b], 0), T);
+  const int s1 = min(max(cu[b + 1], s0), T);
+  return SeqView{s0, min(s1 - s0, N)};
+}
+// First element of the per-row statistics (L, D) of sequence b, head h: [B][H][N] for fixed
+// lengths, [H][T] for packed variable-length batches.
+__device__ __forceinline__ size_t stat_row(const int* cu, int T, int b, int H, int h, const SeqView& sv) {
+  return cu == nullptr ? ((size_t)b * H + h) * sv.len : (size_t)h * T + sv.start;
+}
 
 template <class F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {

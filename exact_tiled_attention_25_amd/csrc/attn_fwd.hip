@@ -157,29 +157,32 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::WAVES, 1) void fwd_kernel(FwdParams
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps loop control scalar
   const int l32 = lane & 31, hf = lane >> 5;
-  const int H = p.H, N = p.N;
-  const int nqt = (N + kBR - 1) / kBR;
+  const int H = p.H;
+  const int nqt = (p.N + kBR - 1) / kBR;   // p.N: the (longest) sequence length
 
   const int work = xcd_remap(blockIdx.x, gridDim.x);
   const int split = SPLIT ? work % p.splits : 0;   // parts of one query tile are neighbours
   const int qwork = SPLIT ? work / p.splits : work;
   const int qi = qwork % nqt;
-  const int bh = qwork / nqt;
+  const int bh = spread_pair(qwork / nqt, p.B * H, !SPLIT && p.cu != nullptr);
   const int h = bh % H, b = bh / H;
+  const SeqView sv = seq_view(p.cu, b, p.N, p.T);
+  const int N = sv.len;
   const int qt = CAUSAL ? nqt - 1 - qi : qi;
+  if (qt * kBR >= N) return;   // a shorter sequence of a variable-length batch: nothing here
   const int q0 = qt * kBR + wave * kQW;
   const int qrow = q0 + l32;
 
   // Per-(batch, head) buffer views: offset = row * row_bytes + byte within the head's row.
   const uint32_t row_bytes = (uint32_t)H * D * 2;
-  const size_t head_off = ((size_t)b * N * H + h) * D * 2;
+  const size_t head_off = ((size_t)sv.start * H + h) * D * 2;
   const uint32_t nrec = (uint32_t)N * row_bytes - (uint32_t)h * D * 2;
   const auto rq = make_rsrc((const char*)p.q + head_off, nrec);
   const auto ro = make_rsrc((const char*)p.o + head_off, nrec);
   // K and V: [B][N][Hkv][D], head h / (H / Hkv) (grouped key/value heads; Hkv = H is plain)
   const int Hkv = p.Hkv, kvh = h / (H / Hkv);
   const uint32_t kv_row_bytes = (uint32_t)Hkv * D * 2;
-  const size_t kv_head_off = ((size_t)b * N * Hkv + kvh) * D * 2;
+  const size_t kv_head_off = ((size_t)sv.start * Hkv + kvh) * D * 2;
   const uint32_t kv_nrec = (uint32_t)N * kv_row_bytes - (uint32_t)kvh * D * 2;
 
   const int kend = CAUSAL ? min(N, (qt + 1) * kBR) : N;
@@ -461,7 +464,7 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::WAVES, 1) void fwd_kernel(FwdParams
                    pack2<BF16>(oacc[i][4 * rr + 2] * inv, oacc[i][4 * rr + 3] * inv)};
         buf_store8(ro, (uint32_t)qrow * row_bytes + d0 * 2, v);
       }
-    if (hf == 0 && qrow < N) p.lse[((size_t)b * H + h) * N + qrow] = (m_use + fast_log2(l_tot)) * kLn2;
+    if (hf == 0 && qrow < N) p.lse[stat_row(p.cu, p.T, b, H, h, sv) + qrow] = (m_use + fast_log2(l_tot)) * kLn2;
   }
 }
 

@@ -14,6 +14,10 @@ struct FwdParams {
   int B, H, N;
   float c;  // softmax scale * log2(e): scores are exponentiated with exp2
   int Hkv;  // key/value heads (divides H); query head h reads key/value head h / (H / Hkv)
+  // variable-length batches: cu_seqlens [B+1] (device) or null; with it, N is the longest
+  // sequence, tensors are packed [T][heads][d] and LSE is [H][T]
+  const int* cu;
+  int T;
   // split-KV only: S = splits part slots per query tile; a query tile with n key tiles
   // uses ceil(n / split_tiles) of them (split_tiles = ceil(ceil(N/64) / S)); the per-part
   // results O_s = O/l (fp32 [S][B][H][N][d]) and L_s (fp32 [S][B][H][N]; -inf: no keys of
@@ -39,6 +43,8 @@ struct BwdParams {
   float scale;
   float c;  // scale * log2(e)
   int Hkv;  // key/value heads (divides H); dK, dV are [B][N][Hkv][d]
+  const int* cu;  // variable-length batches as in FwdParams (then D is [H][T] too)
+  int T;
 };
 
 struct Fp8QuantParams {

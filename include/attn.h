@@ -63,6 +63,31 @@ attn_status_t attn_fwd_gqa(const void* q, const void* k, const void* v, void* o,
                            int B, int H, int H_kv, int N, int d, int causal, float scale,
                            attn_dtype_t dtype, attn_stream_t stream);
 
+/* Variable-length batches (packed): B sequences of lengths cu_seqlens[b+1] - cu_seqlens[b],
+ * stored back to back. q, o: [T][H][d]; k, v: [T][H_kv][d] (H_kv dividing H, grouped as in
+ * attn_fwd_gqa); lse: [H][T] fp32. cu_seqlens is DEVICE memory, B+1 int32 offsets with
+ * 0 = cu[0] <= cu[1] <= ... <= cu[B] = T; max_seqlen >= every length (it sizes the grid).
+ * Each sequence is an independent attention (causal: token i of a sequence sees tokens 0..i
+ * of the same sequence); the enterprise post lists variable-length handling among the
+ * kernel's forthcoming features ("GPU Compatibility and Enablement Matrix"). The offsets are
+ * not read on the host: offsets outside [0, T] or lengths above max_seqlen are clamped, so
+ * they give unspecified results but no access outside the tensors. Errors as attn_fwd, plus
+ * ATTN_EINVAL for negative sizes or a null cu_seqlens. */
+attn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const int* cu_seqlens, int B, int T, int max_seqlen, int H, int H_kv,
+                              int d, int causal, float scale, attn_dtype_t dtype,
+                              attn_stream_t stream);
+
+/* Bytes of device workspace attn_bwd_varlen needs: fp32 D, [H][T]. */
+size_t attn_bwd_varlen_workspace_bytes(int T, int H);
+
+/* Backward of attn_fwd_varlen: layouts as there; dq [T][H][d], dk, dv [T][H_kv][d]. */
+attn_status_t attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                              const int* cu_seqlens, int B, int T, int max_seqlen, int H, int H_kv,
+                              int d, int causal, float scale, attn_dtype_t dtype, void* workspace,
+                              size_t workspace_bytes, attn_stream_t stream);
+
 /* Bytes of device workspace attn_fwd_splitkv needs: per part, O_s fp32 [B][H][N][d] and
  * L_s fp32 [B][H][N] (num_splits * B*H*N*(d+1) * 4 bytes). 0 for invalid arguments. */
 size_t attn_fwd_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits);

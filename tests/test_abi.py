@@ -67,6 +67,15 @@ def test_null_pointers_rejected(lib):
                             None, 0, None) == 1
     assert lib.attn_bwd_gqa(None, None, None, None, None, None, None, None, None, 1, 6, 4, 16, 64, 0, 0.125, 0,
                             None, 0, None) == 1
+    assert lib.attn_fwd_varlen(None, None, None, None, None, None, 2, 100, 64, 4, 2, 64, 0, 0.125, 0, None) == 1
+    assert lib.attn_fwd_varlen(None, None, None, None, None, None, -1, 100, 64, 4, 2, 64, 0, 0.125, 0, None) == 1
+    cu = (ctypes.c_int * 3)(0, 40, 100)  # only checked for null on the host
+    assert lib.attn_fwd_varlen(None, None, None, None, None, cu, 2, 100, 64, 4, 2, 96, 0, 0.125, 0, None) == 2
+    assert lib.attn_fwd_varlen(None, None, None, None, None, cu, 2, 100, 64, 4, 3, 64, 0, 0.125, 0, None) == 1
+    assert lib.attn_fwd_varlen(None, None, None, None, None, None, 2, 0, 64, 4, 2, 64, 0, 0.125, 0, None) == 0
+    assert lib.attn_bwd_varlen(None, None, None, None, None, None, None, None, None, None, 2, 100, 64, 4, 3, 64, 0,
+                               0.125, 0, None, 0, None) == 1
+    assert lib.attn_bwd_varlen_workspace_bytes(100, 4) == 1600
     assert lib.attn_fwd_splitkv(None, None, None, None, None, 1, 1, 16, 64, 0, 0.125, 0, 2, None, 0, None) == 1
     assert lib.attn_fwd_splitkv(None, None, None, None, None, 1, 1, 16, 64, 0, 0.125, 0, 0, None, 0, None) == 1
     assert lib.attn_fwd_splitkv(None, None, None, None, None, 1, 1, 16, 96, 0, 0.125, 0, 2, None, 0, None) == 2
