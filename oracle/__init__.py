@@ -12,6 +12,8 @@ Sources (the three pages about FlashAttention-3):
     "Putting It Together" (the epilogue row).
   * "FlashAttention 3 Hardware Acceleration: Hopper GPU Strategies ..." (enterprise post):
     sections "Online Softmax", "FP8 Accumulation", "FP8 Assumptions".
+  * Rotary position embedding, which the pages only name as fusable with the Hadamard
+    transform, follows Su et al., "RoFormer" (2021); see rope.py.
 
 Pin status of every function is stated in its module docstring; every function here is
 pinned by a ``-m "not gpu"`` test in ``tests/test_oracle_*.py``.
@@ -23,3 +25,5 @@ from .fp8 import (e4m3_decode, e4m3_encode, e4m3_finite_values, splitmix64, hada
                   sylvester_hadamard, rotation_matrix, quantize_blocks, quantize_per_tensor,
                   dequantize_blocks,
                   fp8_emulated_forward, FP8_BLOCK_ROWS, E4M3_MAX)
+from .rope import (apply_rope, rope_frequencies, rope_angles, quantize_rope_blocks,  # noqa: F401
+                   ROPE_BASE)

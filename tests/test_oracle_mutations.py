@@ -180,3 +180,65 @@ def test_fp8_mutation_is_caught(monkeypatch, name):
     monkeypatch.setattr(F, attr, bad)
     monkeypatch.setattr(oracle, attr, bad)
     assert any(_fails(fn, *args) for fn, *args in _fp8_pins()), name
+
+
+from oracle import rope as RP  # noqa: E402
+import test_oracle_rope as TR  # noqa: E402
+
+_ORIG_FREQ = RP.rope_frequencies
+
+
+def _rope_half_split(x, base=RP.ROPE_BASE):
+    """Pairs (x_i, x_{i+d/2}) instead of adjacent pairs."""
+    x = RP._f64(x)
+    d = x.shape[-1]
+    perm = np.stack([np.arange(d // 2), np.arange(d // 2) + d // 2], axis=1).reshape(-1)
+    y = np.empty_like(x)
+    y[..., perm] = _ORIG_ROPE(x[..., perm], base)
+    return y
+
+
+def _rope_negative_angle(x, base=RP.ROPE_BASE):
+    x = RP._f64(x)
+    flip = x.copy()
+    flip[..., 1::2] *= -1
+    y = _ORIG_ROPE(flip, base)
+    y[..., 1::2] *= -1
+    return y
+
+
+def _rope_from_position_one(x, base=RP.ROPE_BASE):
+    x = RP._f64(x)
+    pad = np.concatenate([np.zeros_like(x[:, :1]), x], axis=1)
+    return _ORIG_ROPE(pad, base)[:, 1:]
+
+
+def _freq_exponent_i_over_d(d, base=RP.ROPE_BASE):
+    return np.power(float(base), -np.arange(d // 2, dtype=np.float64) / d)
+
+
+_ORIG_ROPE = RP.apply_rope
+
+ROPE_CASES = {
+    "half-split pairs": ("apply_rope", _rope_half_split),
+    "rotation by minus the angle": ("apply_rope", _rope_negative_angle),
+    "positions start at 1": ("apply_rope", _rope_from_position_one),
+    "frequency exponent i/d": ("rope_frequencies", _freq_exponent_i_over_d),
+}
+
+
+def _rope_pins():
+    return [
+        (TR.test_frequency_table_closed_values,),
+        (TR.test_rope_is_complex_multiplication, 64),
+        (TR.test_rope_is_the_exponential_of_its_generator,),
+        (TR.test_position_zero_is_identity_and_norms_are_kept,),
+        (TR.test_scores_depend_only_on_relative_position,),
+    ]
+
+
+@pytest.mark.parametrize("name", list(ROPE_CASES))
+def test_rope_mutation_is_caught(monkeypatch, name):
+    attr, bad = ROPE_CASES[name]
+    monkeypatch.setattr(RP, attr, bad)
+    assert any(_fails(fn, *args) for fn, *args in _rope_pins()), name
