@@ -22,7 +22,7 @@ FP8_BLOCK = 64
 EXPORTS = ("attn_fwd", "attn_fwd_gqa", "attn_fwd_varlen", "attn_fwd_splitkv_workspace_bytes",
            "attn_fwd_splitkv", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_gqa",
            "attn_bwd_varlen_workspace_bytes", "attn_bwd_varlen", "attn_fp8_quantize",
-           "attn_fp8_quantize_per_tensor", "attn_fwd_fp8", "attn_strerror")
+           "attn_fp8_quantize_per_tensor", "attn_fp8_quantize_rope", "attn_fwd_fp8", "attn_strerror")
 _DTYPE_CODE = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_FP16}
 
 _lib = None
@@ -67,6 +67,8 @@ def load(path=None):
     for fn in (L.attn_fp8_quantize, L.attn_fp8_quantize_per_tensor):
         fn.argtypes = [vp, vp, vp, i, i, i, i, i, i, u64, vp]
         fn.restype = i
+    L.attn_fp8_quantize_rope.argtypes = [vp, vp, vp, i, i, i, i, i, ctypes.c_double, i, u64, vp]
+    L.attn_fp8_quantize_rope.restype = i
     L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, vp, u64, i, vp]
     L.attn_fwd_fp8.restype = i
     L.attn_strerror.argtypes = [i]
@@ -296,6 +298,23 @@ def attn_fp8_quantize(x, rotate, hadamard_seed=0, x8=None, descale=None, stream=
 def attn_fp8_quantize_per_tensor(x, rotate, hadamard_seed=0, x8=None, descale=None, stream=None):
     """attn_fp8_quantize with one descale for the whole tensor."""
     return attn_fp8_quantize(x, rotate, hadamard_seed, x8, descale, stream, per_tensor=True)
+
+
+def attn_fp8_quantize_rope(x, rotate, hadamard_seed=0, rope_base=10000.0, x8=None, descale=None, stream=None):
+    """Fused RoPE (row n of each batch at position n) + optional Hadamard rotation + 64-row
+    block quantisation of x [B, N, H, d]: e4m3 codes and fp32 descales [B, H, ceil(N/64)]."""
+    _tensor(x, "x", dtypes=tuple(_DTYPE_CODE))
+    B, N, H, d = x.shape
+    nblk = (N + FP8_BLOCK - 1) // FP8_BLOCK
+    x8 = (torch.empty(x.shape, dtype=torch.uint8, device=x.device) if x8 is None
+          else _tensor(x8, "x8", x.shape, (torch.uint8,), x.device))
+    descale = (torch.empty((B, H, nblk), dtype=torch.float32, device=x.device) if descale is None
+               else _tensor(descale, "descale", (B, H, nblk), (torch.float32,), x.device))
+    _check("attn_fp8_quantize_rope",
+           load().attn_fp8_quantize_rope(_ptr(x), _ptr(x8), _ptr(descale), B, H, N, d, _DTYPE_CODE[x.dtype],
+                                         float(rope_base), int(bool(rotate)),
+                                         int(hadamard_seed) & (2 ** 64 - 1), _stream(x, stream)))
+    return x8, descale
 
 
 def attn_fwd_fp8(q8, k8, v8, descale_q, descale_k, descale_v, causal=False, scale=None,

@@ -209,8 +209,10 @@ attn_status_t attn_bwd_gqa(const void* q, const void* k, const void* v, const vo
 
 static attn_status_t fp8_quantize(const void* x, uint8_t* x8, float* descale, int B, int H, int N,
                                   int d, attn_dtype_t dtype, int rotate, uint64_t hadamard_seed,
-                                  bool per_tensor, attn_stream_t stream) {
+                                  bool per_tensor, attn_stream_t stream, double rope_base = 0.0) {
   if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_EINVAL;
+  const bool rope = rope_base != 0.0;
+  if (rope && !(std::isfinite(rope_base) && rope_base > 1.0)) return ATTN_EINVAL;
   bool empty = false;
   attn_status_t st = check_sizes(B, H, N, d, &empty);
   if (st != ATTN_OK || empty) return st;
@@ -218,7 +220,8 @@ static attn_status_t fp8_quantize(const void* x, uint8_t* x8, float* descale, in
   if ((double)B * H * ((N + 63) / 64) >= 2147483647.0) return ATTN_EUNSUPPORTED;
   if (!x || !x8 || !descale) return ATTN_EINVAL;
   if ((st = check_device()) != ATTN_OK) return st;
-  attn::Fp8QuantParams p{x, x8, descale, B, H, N, rotate != 0, {0, 0, 0, 0, 0, 0, 0, 0}, per_tensor ? 1 : 0};
+  attn::Fp8QuantParams p{x, x8, descale, B, H, N, rotate != 0, {0, 0, 0, 0, 0, 0, 0, 0}, per_tensor ? 1 : 0,
+                         rope ? 1 : 0, rope ? std::log2(rope_base) : 0.0};
   if (rotate)
     for (int t = 0; t < d; ++t)
       if (splitmix64_output(hadamard_seed, (uint64_t)t) >> 63) p.neg[t >> 5] |= 1u << (t & 31);
@@ -236,6 +239,14 @@ attn_status_t attn_fp8_quantize_per_tensor(const void* x, uint8_t* x8, float* de
                                            int B, int H, int N, int d, attn_dtype_t dtype,
                                            int rotate, uint64_t hadamard_seed, attn_stream_t stream) {
   return fp8_quantize(x, x8, descale, B, H, N, d, dtype, rotate, hadamard_seed, true, stream);
+}
+
+attn_status_t attn_fp8_quantize_rope(const void* x, uint8_t* x8, float* descale,
+                                     int B, int H, int N, int d, attn_dtype_t dtype,
+                                     double rope_base, int rotate, uint64_t hadamard_seed,
+                                     attn_stream_t stream) {
+  if (!(std::isfinite(rope_base) && rope_base > 1.0)) return ATTN_EINVAL;
+  return fp8_quantize(x, x8, descale, B, H, N, d, dtype, rotate, hadamard_seed, false, stream, rope_base);
 }
 
 attn_status_t attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,

@@ -55,7 +55,30 @@ __device__ __forceinline__ float clamp448(float x) { return fminf(fmaxf(x, -kE4m
 // the block's amax (of the rotated values) is written, to the descale slot. kQuantFixed:
 // codes with the descale already in the slot (which is left as it is).
 constexpr int kQuantBlock = 0, kQuantAmax = 1, kQuantFixed = 2;
-template <bool BF16, int D, int MODE>
+// Rotary position embedding of one row's EPT consecutive dims (pairs (2i, 2i+1) with
+// i = first/2 .. ): pair i at position pos turns by pos * theta_i, theta_i = base^(-2i/d).
+// The angle is formed and reduced modulo 2 pi in fp64, so it stays exact to about 1e-12 at
+// any position below 2^31; only its sine and cosine and the 2x2 rotation are fp32.
+template <int D, int EPT>
+__device__ __forceinline__ void rope_row(float (&y)[EPT], int pos, int first, double log2_base) {
+  constexpr double kTwoPi = 6.283185307179586232;    // fp64(2 pi)
+  constexpr double kInvTwoPi = 0.15915494309189534561;
+  double theta = exp2(-(double)first / D * log2_base);
+  const double ratio = exp2(-2.0 / D * log2_base);
+#pragma unroll
+  for (int e = 0; e < EPT; e += 2) {
+    const double ang = (double)pos * theta;
+    const double r = fma(-rint(ang * kInvTwoPi), kTwoPi, ang);
+    float sn, cs;
+    sincosf((float)r, &sn, &cs);
+    const float a = y[e], b = y[e + 1];
+    y[e] = a * cs - b * sn;
+    y[e + 1] = a * sn + b * cs;
+    theta *= ratio;
+  }
+}
+
+template <bool BF16, int D, int MODE, bool ROPE>
 __global__ __launch_bounds__(256) void fp8_quant_kernel(Fp8QuantParams p) {
   constexpr int EPT = D / 4;   // elements per thread (4 threads per row)
   const int tid = threadIdx.x, t = tid & 3, rloc = tid >> 2;
@@ -79,6 +102,7 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(Fp8QuantParams p) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) unpack2q<BF16>(v[w], y[8 * c + 2 * w], y[8 * c + 2 * w + 1]);
   }
+  if constexpr (ROPE) rope_row<D, EPT>(y, row, t * EPT, p.rope_log2_base);
   if (p.rotate) {
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
@@ -536,21 +560,26 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
   }
 }
 
-template <bool BF16, int D>
-hipError_t launch_q(const Fp8QuantParams& p, hipStream_t s) {
+template <bool BF16, int D, bool ROPE>
+hipError_t launch_qr(const Fp8QuantParams& p, hipStream_t s) {
   const int nblk = (p.N + 63) / 64;
   const dim3 grid((unsigned)(p.B * p.H * nblk));
   if (!p.per_tensor) {
-    hipLaunchKernelGGL((fp8_quant_kernel<BF16, D, kQuantBlock>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((fp8_quant_kernel<BF16, D, kQuantBlock, ROPE>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((fp8_quant_kernel<BF16, D, kQuantAmax>), grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((fp8_quant_kernel<BF16, D, kQuantAmax, ROPE>), grid, dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fp8_tensor_scale_kernel, dim3(1), dim3(1024), 0, s, p.descale, p.B * p.H * nblk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((fp8_quant_kernel<BF16, D, kQuantFixed>), grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((fp8_quant_kernel<BF16, D, kQuantFixed, ROPE>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
+}
+
+template <bool BF16, int D>
+hipError_t launch_q(const Fp8QuantParams& p, hipStream_t s) {
+  return p.rope ? launch_qr<BF16, D, true>(p, s) : launch_qr<BF16, D, false>(p, s);
 }
 
 template <bool OUT_BF16, int D, bool CAUSAL>

@@ -55,6 +55,8 @@ struct Fp8QuantParams {
   int rotate;
   uint32_t neg[8];  // bit t set: dim t of the random sign vector is -1 (d <= 256)
   int per_tensor;   // one descale for the whole tensor instead of one per 64-row block
+  int rope;         // rotary position embedding of each row (position = row index) first
+  double rope_log2_base;  // log2 of the RoPE base: pair i turns by n * base^(-2i/d)
 };
 
 struct Fp8FwdParams {

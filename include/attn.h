@@ -157,12 +157,29 @@ attn_status_t attn_fp8_quantize_per_tensor(const void* x, uint8_t* x8, float* de
                                            int rotate, uint64_t hadamard_seed,
                                            attn_stream_t stream);
 
+/* Fused prologue: rotary position embedding, then the random-sign Hadamard rotation, then
+ * 64-row block quantisation, in one pass over x ("FP8 accuracy controls": the Hadamard
+ * transform can be fused with rotary embedding; the enterprise post names the same fusion).
+ * The pages do not define the embedding; it is RoPE as in Su et al., "RoFormer" (2021): the
+ * row at position n (its index 0 .. N-1 within its batch) has each pair of dims (2i, 2i+1)
+ * turned by the angle n * rope_base^(-2i/d): (a, b) -> (a cos - b sin, a sin + b cos).
+ * Apply it to Q and K with the same seed (attention then sees the scores of RoPE attention;
+ * V takes attn_fp8_quantize with rotate = 0). Arguments, codes and descales otherwise as
+ * attn_fp8_quantize. rope_base must be finite and > 1 (ATTN_EINVAL otherwise; 10000 is the
+ * usual value). Angles are reduced modulo 2 pi in fp64; sine, cosine and the pair rotation
+ * are fp32. */
+attn_status_t attn_fp8_quantize_rope(const void* x, uint8_t* x8, float* descale,
+                                     int B, int H, int N, int d, attn_dtype_t dtype,
+                                     double rope_base, int rotate, uint64_t hadamard_seed,
+                                     attn_stream_t stream);
+
 /* FP8 forward attention ("FP8 layout conformance", "FP8 accuracy controls"):
  * O = softmax(scale * Qh Kh^T [+ mask]) Vh with Xh = e4m3(X8) * descale_X per 64-row block.
  * Q8 and K8 must have been rotated with the same seed (or both not at all); because the
  * rotation is orthogonal the scores do not depend on it, and `hadamard_seed` is carried
- * only to describe the inputs. The probabilities are rounded to e4m3 (scaled by 2^8) for
- * the P V product. O is written in `out_dtype`, LSE in fp32 (natural log). */
+ * only to describe the inputs. The probabilities are rounded to e4m3 for the P V product,
+ * scaled by 64 * dv/dv_max (dv the V descale of the key's block, dv_max the head's largest);
+ * the epilogue undoes that factor exactly. O is written in `out_dtype`, LSE in fp32 (natural log). */
 attn_status_t attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                            void* o, float* lse, int B, int H, int N, int d, int causal,
                            float scale, const float* descale_q, const float* descale_k,

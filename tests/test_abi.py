@@ -60,6 +60,12 @@ def test_null_pointers_rejected(lib):
                         None, 0, None) == 1
     assert lib.attn_fp8_quantize(None, None, None, 1, 1, 16, 64, 0, 1, 0, None) == 1
     assert lib.attn_fp8_quantize_per_tensor(None, None, None, 1, 1, 16, 64, 0, 1, 0, None) == 1
+    assert lib.attn_fp8_quantize_rope(None, None, None, 1, 1, 16, 64, 0, 10000.0, 1, 0, None) == 1
+    # RoPE base: finite and above 1, checked before pointers or the device
+    for base in (1.0, 0.5, -10000.0, float("nan"), float("inf")):
+        assert lib.attn_fp8_quantize_rope(None, None, None, 1, 1, 16, 64, 0, base, 1, 0, None) == 1
+    assert lib.attn_fp8_quantize_rope(None, None, None, 1, 1, 16, 96, 0, 10000.0, 1, 0, None) == 2
+    assert lib.attn_fp8_quantize_rope(None, None, None, 0, 1, 16, 64, 0, 10000.0, 1, 0, None) == 0
     assert lib.attn_fwd_gqa(None, None, None, None, None, 1, 4, 2, 16, 64, 0, 0.125, 0, None) == 1
     assert lib.attn_fwd_gqa(None, None, None, None, None, 1, 4, 3, 16, 64, 0, 0.125, 0, None) == 1
     assert lib.attn_fwd_gqa(None, None, None, None, None, 1, 4, 0, 16, 64, 0, 0.125, 0, None) == 1
