@@ -194,9 +194,11 @@ constexpr int kBC8 = 64;              // keys per tile: one K and one V scale bl
 constexpr float kTau8 = 2.0f;         // lazy-rescale threshold (log2 units)
 constexpr float kPScale = 64.0f;      // P~ * 64 * dv/dv_max is the fp8 PV operand
 constexpr float kLn2 = 0.69314718055994530942f;
-// K and V tiles: row-major e4m3 rows of D bytes at pitch D + 16 (16-byte row offset mod
-// 256: the K row reads of a 16-lane group and the V transpose reads are conflict-free).
+// K tiles: row-major e4m3 rows of D bytes at pitch D + 16 (the K row reads of a 16-lane
+// group fall on disjoint banks). V tiles: pitch D + 32 with rows exchanged by swap23 (see
+// vt8_lane_off), which makes the transpose reads conflict-free.
 template <int D> __host__ __device__ constexpr int f8_pitch() { return D + 16; }
+template <int D> __host__ __device__ constexpr int f8_vpitch() { return D + 32; }
 
 __device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
@@ -218,10 +220,14 @@ __device__ __forceinline__ i32x8 lds_k8(const char* lane_base, int kb, int ks) {
 // 32*(b/16) + 8*((b%16)/4) + 4*h + b%4; so source lane s of read j points at key
 // 16j + 8*(s/8) + 4*h + (s/2)%4 and dims 16*((l/16)%2) + 8*(s%2), and lane l receives dim
 // l%32 (plus 32*i for output block i) of exactly the keys of its P bytes 8j .. 8j+7.
+// The tile's rows are stored exchanged by swap23, so key 16j + 8a + 4h + c sits at LDS row
+// 16j + 8h + 4a + c: the 32 lanes of one half (one LDS pass of 8-byte reads) gather 8
+// consecutive rows, 32 bytes each, and at a pitch of D + 32 bytes (an odd multiple of 32
+// modulo 256) those 8 pieces cover all 64 banks once.
 template <int P>
 __device__ __forceinline__ int vt8_lane_off(int lane) {
   const int s = lane & 15, h = lane >> 5;
-  return (8 * (s >> 3) + 4 * h + ((s >> 1) & 3)) * P + 16 * ((lane >> 4) & 1) + 8 * (s & 1);
+  return (8 * h + 4 * (s >> 3) + ((s >> 1) & 3)) * P + 16 * ((lane >> 4) & 1) + 8 * (s & 1);
 }
 template <int P>
 __device__ __forceinline__ i32x8 lds_vt8(const char* lane_base, int i) {
@@ -258,11 +264,13 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
   constexpr int NKB = BC / 32;       // 32-key score blocks per tile
   constexpr int NKS = D / 64;        // k-steps of the score product
   constexpr int NDB = D / 32;        // 32-dim output blocks
-  constexpr int P8 = f8_pitch<D>();
+  constexpr int P8 = f8_pitch<D>(), PV8 = f8_vpitch<D>();
   using Plan = DmaPlanBytes<D, BC, P8, kWaves>;
-  constexpr int TB = Plan::BYTES;
+  using VPlan = DmaPlanBytes<D, BC, PV8, kWaves>;
+  constexpr int TB = Plan::BYTES, TBV = VPlan::BYTES;
   constexpr int KMIN = Plan::NI / kWaves;   // may be 0 (small tiles): such waves issue no DMA
-  __shared__ __attribute__((aligned(1024))) char smem[2 * NS * TB];
+  constexpr int KMINV = VPlan::NI / kWaves;
+  __shared__ __attribute__((aligned(1024))) char smem[NS * (TB + TBV)];
   __shared__ float red[kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -321,23 +329,26 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
   auto is_edge = [&](int j) { const int k0 = j * BC; return (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0); };
   // Stage offsets pass through readfirstlane: opaque to loop strength reduction.
   auto kst = [&](int j) { return smem + __builtin_amdgcn_readfirstlane((j % NS) * TB); };
-  auto vst = [&](int j) { return smem + NS * TB + __builtin_amdgcn_readfirstlane((j % NS) * TB); };
-  uint32_t voff[Plan::NPW];
+  auto vst = [&](int j) { return smem + NS * TB + __builtin_amdgcn_readfirstlane((j % NS) * TBV); };
+  uint32_t voff[Plan::NPW], vvoff[VPlan::NPW];
   dma_init<Plan, kWaves>(voff, row_bytes, wave, lane);
+  dma_init<VPlan, kWaves, 0, true>(vvoff, row_bytes, wave, lane);
   const char* kbase = (const char*)p.k8 + head_off;
   const char* vbase = (const char*)p.v8 + head_off;
   auto dma_k = [&](int t) { dma_issue<Plan, kWaves>(voff, kst(t), kbase, t * BC, row_bytes, nrec, wave); };
-  auto dma_v = [&](int t) { dma_issue<Plan, kWaves>(voff, vst(t), vbase, t * BC, row_bytes, nrec, wave); };
+  auto dma_v = [&](int t) { dma_issue<VPlan, kWaves>(vvoff, vst(t), vbase, t * BC, row_bytes, nrec, wave); };
 
   // DMA schedule as in the bf16 forward: the prologue requests K(0), then V(t), K(t+1) for
   // t = 0 .. NS-2; iteration j requests V(j+NS-1), K(j+NS); before iteration j, K(j+1) and
   // V(j) must have landed.
-  const int n_w = KMIN + (wave < Plan::NI % kWaves ? 1 : 0);   // this wave's DMA share per tile
-  constexpr int KEEP_MAX = (NS - 2) * 2 * (KMIN + 1);
+  // this wave's DMA instructions per K tile and per V tile
+  const int n_w = KMIN + (wave < Plan::NI % kWaves ? 1 : 0);
+  const int n_wv = KMINV + (wave < VPlan::NI % kWaves ? 1 : 0);
+  constexpr int KEEP_MAX = (NS - 2) * (KMIN + KMINV + 2);
   auto wait_before = [&](int j) {
     int keep = 0;
 #pragma unroll
-    for (int t = 1; t <= NS - 2; ++t) keep += (j + t < nkt ? n_w : 0) + (j + t + 1 < nkt ? n_w : 0);
+    for (int t = 1; t <= NS - 2; ++t) keep += (j + t < nkt ? n_wv : 0) + (j + t + 1 < nkt ? n_w : 0);
     wait_dma_keep_rt<KEEP_MAX>(keep);
   };
   // per-tile descale factors, loaded one tile ahead (before that iteration's DMA batch)
@@ -359,7 +370,7 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
 #pragma unroll
   for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
-  const int k_lane = k8_lane_off<P8>(lane), v_lane = vt8_lane_off<P8>(lane);
+  const int k_lane = k8_lane_off<P8>(lane), v_lane = vt8_lane_off<PV8>(lane);
 
   wait_before(0);
   __syncthreads();
@@ -466,10 +477,10 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
     i32x8 vop[S2];
     float mx = -INFINITY, psum = 0.f;
 #pragma unroll
-    for (int t = 0; t < PF && t < S2; ++t) vop[t] = lds_vt8<P8>(vc, t);
+    for (int t = 0; t < PF && t < S2; ++t) vop[t] = lds_vt8<PV8>(vc, t);
 #pragma unroll
     for (int t = 0; t < S2; ++t) {
-      if (t + PF < S2) vop[t + PF] = lds_vt8<P8>(vc, t + PF);
+      if (t + PF < S2) vop[t + PF] = lds_vt8<PV8>(vc, t + PF);
       oacc[t] = mfma_f8(vop[t], pk, oacc[t]);
 #pragma unroll
       for (int u = 0; u < MPS; u += 2) {
@@ -530,7 +541,7 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
       l_run = fmaf(psum, 1.0f / wgt, l_run);
       const char* vc = vst(j) + v_lane;
 #pragma unroll
-      for (int i = 0; i < NDB; ++i) oacc[i] = mfma_f8(lds_vt8<P8>(vc, i), pk, oacc[i]);
+      for (int i = 0; i < NDB; ++i) oacc[i] = mfma_f8(lds_vt8<PV8>(vc, i), pk, oacc[i]);
       if (j + 1 < nkt_w) {
         tile_scores(sc, kst(j + 1) + k_lane);
         if (is_edge(j + 1)) tile_mask(sc, (j + 1) * BC);

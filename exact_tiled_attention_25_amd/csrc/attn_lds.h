@@ -58,14 +58,20 @@ __host__ __device__ constexpr int swz(int r) {
   return SWZ == 0 ? 0 : SWZ == 64 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) : (((r & 3) << 2) | ((r >> 2) & 3));
 }
 
-template <class Plan, int NWAVES, int SWZ = 0>
+// SWAP23: LDS row r holds source row r with bits 2 and 3 exchanged (an involution that
+// stays inside each 16-row group), so the rows a transpose read gathers can be made to sit
+// at consecutive LDS rows.
+__host__ __device__ constexpr int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+template <class Plan, int NWAVES, int SWZ = 0, bool SWAP23 = false>
 __device__ __forceinline__ void dma_init(uint32_t* voff, uint32_t row_bytes, int wave, int lane) {
 #pragma unroll
   for (int t = 0; t < Plan::NPW; ++t) {
     const int blk = wave + NWAVES * t;
     const int g = blk * 64 + lane;
     const int r = g / Plan::CPRP, cp = g % Plan::CPRP;
-    voff[t] = (blk < Plan::NI && g < Plan::SLOTS && cp < Plan::CPR) ? (uint32_t)r * row_bytes + (cp ^ swz<SWZ>(r)) * 16
+    const int src = SWAP23 ? swap23(r) : r;
+    voff[t] = (blk < Plan::NI && g < Plan::SLOTS && cp < Plan::CPR) ? (uint32_t)src * row_bytes + (cp ^ swz<SWZ>(r)) * 16
                                                                      : 0x80000000u;
   }
 }
