@@ -270,7 +270,12 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
   constexpr int TB = Plan::BYTES, TBV = VPlan::BYTES;
   constexpr int KMIN = Plan::NI / kWaves;   // may be 0 (small tiles): such waves issue no DMA
   constexpr int KMINV = VPlan::NI / kWaves;
-  __shared__ __attribute__((aligned(1024))) char smem[NS * (TB + TBV)];
+  // Ping-pong (two waves per SIMD): the second wave of each SIMD runs the P~V half of every
+  // fast tile one barrier interval late, so that on each SIMD one wave exponentiates while
+  // the other multiplies; V(j) is then read one interval later, which one more V stage covers.
+  constexpr bool PP = kWaves == 8;
+  constexpr int VS = NS + (PP ? 1 : 0);
+  __shared__ __attribute__((aligned(1024))) char smem[NS * TB + VS * TBV];
   __shared__ float red[kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -329,7 +334,7 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
   auto is_edge = [&](int j) { const int k0 = j * BC; return (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0); };
   // Stage offsets pass through readfirstlane: opaque to loop strength reduction.
   auto kst = [&](int j) { return smem + __builtin_amdgcn_readfirstlane((j % NS) * TB); };
-  auto vst = [&](int j) { return smem + NS * TB + __builtin_amdgcn_readfirstlane((j % NS) * TBV); };
+  auto vst = [&](int j) { return smem + NS * TB + __builtin_amdgcn_readfirstlane((j % VS) * TBV); };
   uint32_t voff[Plan::NPW], vvoff[VPlan::NPW];
   dma_init<Plan, kWaves>(voff, row_bytes, wave, lane);
   dma_init<VPlan, kWaves, 0, true>(vvoff, row_bytes, wave, lane);
@@ -358,6 +363,16 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
   };
   float dk_c, dv_c;   // descales of the tile the next iteration exponentiates
   load_desc(0, dk_c, dv_c);
+  // The weight 64 * dv/dv_max of that tile's P~ enters the exp2 argument as its log2, and
+  // the row sum takes the unweighted P~ through its reciprocal; both are formed one tile
+  // ahead, off the path from the tile barrier to the first exponential.
+  const float inv_dvm = 1.0f / dvm;
+  float logw_c, rw_c;
+  auto set_weight = [&](float dv) {
+    const float w = kPScale * dv * inv_dvm;
+    logw_c = fast_log2(w);
+    rw_c = __builtin_amdgcn_rcpf(w);
+  };
 
   dma_k(0);
 #pragma unroll
@@ -366,6 +381,7 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
     if (t + 1 < nkt) dma_k(t + 1);
   }
 
+  set_weight(dv_c);
   f32x16 oacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
@@ -446,12 +462,11 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
   constexpr int PF = 2;
   static_assert(EPS * S1 == 16 * NKB && MPS * S2 == 16 * NKB && EPS % 4 == 0 && MPS % 2 == 0, "step split");
   float dk_n, dv_n;
-  auto fast_iter = [&](int jj, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) {
+  auto fast_iter = [&](auto late, int jj, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) __attribute__((always_inline)) {
     load_desc(jj + 1 < nkt ? jj + 1 : jj, dk_n, dv_n);
     prefetch(jj);
     rescale();
-    const float wgt = kPScale * (dv_c / dvm);
-    const float bias = fast_log2(wgt) - m_run;
+    const float bias = logw_c - m_run;
     const char* kn = kst(jj + 1) + k_lane;
     const char* vc = vst(jj) + v_lane;
     i32x8 pk;
@@ -473,6 +488,8 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    // late waves: the barrier that ends this tile comes between the two blocks
+    if constexpr (decltype(late)::value) end_tile(jj);
     const float coef_n = cq * dk_n;
     i32x8 vop[S2];
     float mx = -INFINITY, psum = 0.f;
@@ -492,25 +509,31 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
       pin(psum);
       __builtin_amdgcn_sched_barrier(0);
     }
-    l_run = fmaf(psum, 1.0f / wgt, l_run);
+    l_run = fmaf(psum, rw_c, l_run);
     mx = xhalf_max(mx);
     mx_next = mx * coef_n;
     coef_c = coef_n;
     dk_c = dk_n;
     dv_c = dv_n;
-    end_tile(jj);
+    set_weight(dv_c);
+    if constexpr (!decltype(late)::value) end_tile(jj);
   };
   int j = 0;
-  for (; j + 2 < nkt_w && !is_edge(j + 2); j += 2) {
-    fast_iter(j, sc, sn);
-    fast_iter(j + 1, sn, sc);
-  }
-  if (j + 1 < nkt_w && !is_edge(j + 1)) {
-    fast_iter(j, sc, sn);
+  auto fast_loop = [&](auto late) __attribute__((always_inline)) {
+    for (; j + 2 < nkt_w && !is_edge(j + 2); j += 2) {
+      fast_iter(late, j, sc, sn);
+      fast_iter(late, j + 1, sn, sc);
+    }
+    if (j + 1 < nkt_w && !is_edge(j + 1)) {
+      fast_iter(late, j, sc, sn);
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) sc[kb] = sn[kb];
-    ++j;
-  }
+      for (int kb = 0; kb < NKB; ++kb) sc[kb] = sn[kb];
+      ++j;
+    }
+  };
+  // Waves w and w + kWaves/2 share a SIMD (waves are placed on the SIMDs round-robin).
+  if (PP && wave >= kWaves / 2) fast_loop(std::true_type{});
+  else fast_loop(std::false_type{});
   // Remaining tiles, in order: masked tiles and the tail of the key range (waves with
   // nothing left to compute only take part in the ring bookkeeping).
   for (; j < nkt; ++j) {
@@ -519,8 +542,7 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
     if (j < nkt_w) {
       rescale();
       const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      const float wgt = kPScale * (dv_c / dvm);
-      const float bias = fast_log2(wgt) - m_use;
+      const float bias = logw_c - m_use;
       const bool edge = is_edge(j);
       i32x8 pk;
       float psum = 0.f;
@@ -538,7 +560,7 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
           }
           pk[4 * kb + r4] = (int)cvt4_fp8(e4[0], e4[1], e4[2], e4[3]);
         }
-      l_run = fmaf(psum, 1.0f / wgt, l_run);
+      l_run = fmaf(psum, rw_c, l_run);
       const char* vc = vst(j) + v_lane;
 #pragma unroll
       for (int i = 0; i < NDB; ++i) oacc[i] = mfma_f8(lds_vt8<PV8>(vc, i), pk, oacc[i]);
@@ -551,6 +573,7 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
     coef_c = cq * dk_n;
     dk_c = dk_n;
     dv_c = dv_n;
+    set_weight(dv_c);
     end_tile(j);
   }
 
