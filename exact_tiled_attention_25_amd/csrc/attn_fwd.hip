@@ -44,16 +44,24 @@ namespace attn {
 
 namespace {
 
-template <int D> struct FwdCfg;
-// BC: keys per tile; WAVES: waves per workgroup (one workgroup per CU); STAGES: depth of
-// the K ring (the V ring has one more stage under ping-pong).
-// PP: ping-pong schedule between the two waves of each SIMD (needs two waves per SIMD).
-template <> struct FwdCfg<64> { static constexpr int BC = 64, WAVES = 8, STAGES = 3; static constexpr bool PP = true; };
-template <> struct FwdCfg<128> { static constexpr int BC = 64, WAVES = 8, STAGES = 3; static constexpr bool PP = true; };
-template <> struct FwdCfg<256> { static constexpr int BC = 64, WAVES = 4, STAGES = 2; static constexpr bool PP = false; };
+template <int D, bool SMALL = false> struct FwdCfg;
+// BC: keys per tile; WAVES: waves per workgroup; STAGES: depth of the K ring (the V ring has
+// one more stage under ping-pong); PP: ping-pong schedule between the two waves of each
+// SIMD (needs two waves per SIMD); WGS: workgroups per CU.
+// The default form is one workgroup per CU (two waves per SIMD at d <= 128). SMALL is for
+// grids too short to keep one such workgroup per CU busy (short sequences, few heads): half
+// the query rows per workgroup and two workgroups per CU, so that one workgroup's start-up
+// loads and epilogue overlap the other's tiles and twice as many CUs get work.
+template <> struct FwdCfg<64> { static constexpr int BC = 64, WAVES = 8, STAGES = 3, WGS = 1; static constexpr bool PP = true; };
+template <> struct FwdCfg<128> { static constexpr int BC = 64, WAVES = 8, STAGES = 3, WGS = 1; static constexpr bool PP = true; };
+template <> struct FwdCfg<256> { static constexpr int BC = 64, WAVES = 4, STAGES = 2, WGS = 1; static constexpr bool PP = false; };
+template <> struct FwdCfg<64, true> { static constexpr int BC = 64, WAVES = 4, STAGES = 2, WGS = 2; static constexpr bool PP = false; };
+template <> struct FwdCfg<128, true> { static constexpr int BC = 64, WAVES = 4, STAGES = 2, WGS = 2; static constexpr bool PP = false; };
 
 constexpr int kQW = 32;                  // query rows per wave
-template <int D> constexpr int fwd_rows() { return FwdCfg<D>::WAVES * kQW; }   // per workgroup
+template <int D, bool SMALL = false> constexpr int fwd_rows() { return FwdCfg<D, SMALL>::WAVES * kQW; }   // per workgroup
+template <int D, bool SMALL> constexpr int fwd_threads() { return 64 * FwdCfg<D, SMALL>::WAVES; }
+template <int D, bool SMALL> constexpr int fwd_wgs() { return FwdCfg<D, SMALL>::WGS; }
 constexpr float kTau = 8.0f;             // lazy-rescale threshold (log2 units)
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -128,15 +136,16 @@ __device__ __forceinline__ void tile_pv(f32x16 (&oacc)[D / 32], const char* vl, 
 // p.split_tiles) of its query tile's key tiles; slots past the tile's last part exit at
 // once. With two or more parts it writes the part's O/l and L (natural log) to p.o_part,
 // p.lse_part (rows with no key in the part: L = -inf); a tile with one part writes O, L.
-template <bool BF16, int D, bool CAUSAL, bool SPLIT = false>
-__global__ __launch_bounds__(64 * FwdCfg<D>::WAVES, 1) void fwd_kernel(FwdParams p) {
-  constexpr int BC = FwdCfg<D>::BC;
+template <bool BF16, int D, bool CAUSAL, bool SPLIT = false, bool SMALL = false>
+__global__ __launch_bounds__((fwd_threads<D, SMALL>()), (fwd_wgs<D, SMALL>())) void fwd_kernel(FwdParams p) {
+  using Cfg = FwdCfg<D, SMALL>;
+  constexpr int BC = Cfg::BC;
   constexpr int NKB = BC / 32;
   constexpr int NDB = D / 32;
   constexpr int NKS = D / 16;
-  constexpr int kWaves = FwdCfg<D>::WAVES;
-  constexpr int NS = FwdCfg<D>::STAGES;
-  constexpr int kBR = fwd_rows<D>();
+  constexpr int kWaves = Cfg::WAVES;
+  constexpr int NS = Cfg::STAGES;
+  constexpr int kBR = fwd_rows<D, SMALL>();
   using KPlan = DmaPlan<D, BC, k_pitch<D>(), kWaves>;
   using VPlan = DmaPlan<D, BC, v_pitch<D>(), kWaves>;
   // DMA instructions every wave issues per K / V tile (some issue one more)
@@ -146,7 +155,7 @@ __global__ __launch_bounds__(64 * FwdCfg<D>::WAVES, 1) void fwd_kernel(FwdParams
   // Ping-pong: the second wave of each SIMD runs the P~V half of every fast tile one
   // barrier interval late, so that on each SIMD one wave exponentiates while the other
   // multiplies.
-  constexpr bool PP = FwdCfg<D>::PP;
+  constexpr bool PP = Cfg::PP;
   constexpr int VS = NS + (PP ? 1 : 0);
   // K ring (NS stages) then V ring (VS stages); tile t lives in stage t % NS (t % VS).
   // Loop iteration j reads K(j+1) and V(j) (and V(j-1) in the late waves), and requests
@@ -526,12 +535,23 @@ hipError_t launch_split(const FwdParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <bool BF16, int D, bool CAUSAL, bool SMALL>
+hipError_t launch_g(const FwdParams& p, hipStream_t s) {
+  const int nqt = (p.N + fwd_rows<D, SMALL>() - 1) / fwd_rows<D, SMALL>();
+  const dim3 grid((unsigned)(p.B * p.H * nqt));
+  hipLaunchKernelGGL((fwd_kernel<BF16, D, CAUSAL, false, SMALL>), grid, dim3(64 * FwdCfg<D, SMALL>::WAVES), 0, s, p);
+  return hipGetLastError();
+}
+
+// The small form when sequences are short (a workgroup's start-up is a large share of its
+// work) or the default grid would leave CUs idle (fewer workgroups than the 256 CUs).
 template <bool BF16, int D, bool CAUSAL>
 hipError_t launch_t(const FwdParams& p, hipStream_t s) {
-  const int nqt = (p.N + fwd_rows<D>() - 1) / fwd_rows<D>();
-  const dim3 grid((unsigned)(p.B * p.H * nqt));
-  hipLaunchKernelGGL((fwd_kernel<BF16, D, CAUSAL>), grid, dim3(64 * FwdCfg<D>::WAVES), 0, s, p);
-  return hipGetLastError();
+  if constexpr (D <= 128) {
+    const long nwg = (long)p.B * p.H * ((p.N + fwd_rows<D>() - 1) / fwd_rows<D>());
+    if (p.N <= 1024 || nwg < 256) return launch_g<BF16, D, CAUSAL, true>(p, s);
+  }
+  return launch_g<BF16, D, CAUSAL, false>(p, s);
 }
 
 template <bool BF16, int D>
