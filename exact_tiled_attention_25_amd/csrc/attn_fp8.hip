@@ -104,11 +104,18 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(Fp8QuantParams p) {
   }
   if constexpr (ROPE) rope_row<D, EPT>(y, row, t * EPT, p.rope_log2_base);
   if (p.rotate) {
+    // this thread's sign bits: dims t*EPT .. +EPT-1, bit e of word e/32 (EPT/32 words, or the
+    // right half of one word when EPT = 16)
+    constexpr int NW = (EPT + 31) / 32;
+    uint32_t sw[NW];
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const int idx = t * EPT + e;
-      if ((p.neg[idx >> 5] >> (idx & 31)) & 1u) y[e] = -y[e];
+    for (int k = 0; k < NW; ++k) {
+      const int b0 = t * EPT + 32 * k;
+      sw[k] = p.neg[b0 >> 5] >> (b0 & 31);
     }
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+      y[e] = __uint_as_float(__float_as_uint(y[e]) ^ ((sw[e >> 5] << (31 - (e & 31))) & 0x80000000u));
     // Sylvester Hadamard in natural order: pair (i, i + len) -> (x_i + x_j, x_i - x_j).
 #pragma unroll
     for (int len = 1; len < EPT; len <<= 1)
@@ -119,13 +126,20 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(Fp8QuantParams p) {
           y[i] = a + c;
           y[i + len] = a - c;
         }
+    // the last two stages pair the row's 4 lanes (a quad): lane t^1, then lane t^2, read
+    // with DPP quad permutations; the lane with bit m set keeps the difference
+    {
+      const float sg = (t & 1) ? -1.0f : 1.0f;
 #pragma unroll
-    for (int m = 1; m < 4; m <<= 1)
+      for (int e = 0; e < EPT; ++e)
+        y[e] = fmaf(sg, y[e], __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y[e]), 0xB1, 0xF, 0xF, false)));
+    }
+    {
+      const float sg = (t & 2) ? -1.0f : 1.0f;
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        const float o = __shfl_xor(y[e], m);
-        y[e] = (t & m) ? o - y[e] : y[e] + o;
-      }
+      for (int e = 0; e < EPT; ++e)
+        y[e] = fmaf(sg, y[e], __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y[e]), 0x4E, 0xF, 0xF, false)));
+    }
     const float inv_sqrt_d = (D == 64) ? 0.125f : (D == 256) ? 0.0625f : 0.088388347648318440550f;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) y[e] *= inv_sqrt_d;
@@ -151,11 +165,17 @@ __global__ __launch_bounds__(256) void fp8_quant_kernel(Fp8QuantParams p) {
     descale = amax > 0.f ? amax / kE4m3Max : 1.0f;
   }
 
+  // y / descale, correctly rounded to fp32: the product with the fp64 reciprocal carries a
+  // relative error below 2^-52, while a quotient of two fp32 numbers lies at least about
+  // 2^-49 (relative) from any fp32 rounding boundary, so rounding that product to fp32 gives
+  // the IEEE quotient.
+  const double rds = 1.0 / (double)descale;
+  auto quot = [&](float v) { return (float)((double)v * rds); };
   uint32_t codes[EPT / 4];
 #pragma unroll
   for (int w = 0; w < EPT / 4; ++w)
-    codes[w] = cvt4_fp8(clamp448(y[4 * w] / descale), clamp448(y[4 * w + 1] / descale),
-                        clamp448(y[4 * w + 2] / descale), clamp448(y[4 * w + 3] / descale));
+    codes[w] = cvt4_fp8(clamp448(quot(y[4 * w])), clamp448(quot(y[4 * w + 1])),
+                        clamp448(quot(y[4 * w + 2])), clamp448(quot(y[4 * w + 3])));
 #pragma unroll
   for (int c = 0; c < EPT / 16; ++c)
     buf_store16(r8, (uint32_t)row * H * D + t * EPT + 16 * c,
