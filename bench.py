@@ -12,6 +12,12 @@ timed steps. `roofline` describes the kernel with the largest share of the step 
 `cpu_baseline` times the fp64 oracle on a bounded sample of the same work on the host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       [--workload NAME [--seq-len N] [--forward-only]]
+The default is the workload above. --workload picks another shape of the workload table
+(workloads.CONFIGS; its dtype and mask), --seq-len overrides its N (the long-context sweep),
+and --forward-only times attn_fwd alone (the short-sequence and small-d cases, for rocprofv3
+counter runs); stored HBM counters and the CPU baseline are only reported for the default
+workload.
 """
 import argparse
 import hashlib
@@ -37,6 +43,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8, help="heads of the workload timed on the oracle")
+    ap.add_argument("--workload", default=None, help="a workloads.CONFIGS name instead of the default workload")
+    ap.add_argument("--seq-len", type=int, default=None, help="override N of --workload")
+    ap.add_argument("--forward-only", action="store_true", help="time attn_fwd alone")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
@@ -54,8 +63,9 @@ def source_hash():
 
 
 def stored_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary,
-    or None when the summary is missing or was taken on different kernel sources."""
+    """HBM bytes per launch of `kernel` (default workload) from the committed rocprofv3
+    counter summary, or None when the summary is missing or was taken on different kernel
+    sources."""
     try:
         rec = json.load(open(PROFILE_COUNTERS))
     except (OSError, ValueError):
@@ -80,9 +90,24 @@ def main():
 
     binding.load()
     dev = torch.device("cuda:0")
-    w = WORKLOAD
-    B, N, H, d, causal = w["B"], w["N"], w["H"], w["d"], w["causal"]
-    x = workloads.make_inputs(B, N, H, d, w["dtype"], w["seed"], with_do=True)
+    default = args.workload is None and args.seq_len is None and not args.forward_only
+    if args.workload is None:
+        w = dict(WORKLOAD)
+        wname = "attention B=2 N=8192 H=16 d=128 non-causal"
+    else:
+        c = workloads.CONFIGS[args.workload]
+        w = dict(B=c["B"], N=c["N"], H=c["H"], d=c["d"], causal=c["causal"][0], dtype=c["dtype"], seed=c["seed"],
+                 input_scale=c.get("input_scale", 1.0))
+        wname = args.workload
+    if args.seq_len is not None:
+        w["N"] = args.seq_len
+    B, N, H, d, causal, dt = w["B"], w["N"], w["H"], w["d"], w["causal"], w["dtype"]
+    if not default:
+        wname = (f"attention {wname}: B={B} N={N} H={H} d={d} {dt} {'causal' if causal else 'non-causal'}"
+                 + (", forward only" if args.forward_only else ""))
+    else:
+        wname += ": bf16 fwd + bwd, fp8 quantize + fwd"
+    x = workloads.make_inputs(B, N, H, d, dt, w["seed"], w.get("input_scale", 1.0), with_do=True)
     q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
     F = 4.0 * B * H * N * N * d * (0.5 if causal else 1.0)
     seed = 0x5EED
@@ -100,10 +125,10 @@ def main():
     # component name -> (callable, counted flops, algorithmic HBM bytes, peak key)
     elem = B * N * H * d
     comps = {
-        "attn_fwd_bf16": (lambda: binding.attn_fwd(q, k, v, causal, o=o, lse=lse), F,
-                          4 * elem * 2 + B * H * N * 4, "bf16"),
-        "attn_bwd_bf16": (lambda: binding.attn_bwd(q, k, v, o, lse, do, causal, dq=dq, dk=dk, dv=dv, workspace=ws),
-                          2.5 * F, 8 * elem * 2 + B * H * N * 4 * 3, "bf16"),
+        f"attn_fwd_{dt}": (lambda: binding.attn_fwd(q, k, v, causal, o=o, lse=lse), F,
+                           4 * elem * 2 + B * H * N * 4, dt),
+        f"attn_bwd_{dt}": (lambda: binding.attn_bwd(q, k, v, o, lse, do, causal, dq=dq, dk=dk, dv=dv, workspace=ws),
+                           2.5 * F, 8 * elem * 2 + B * H * N * 4 * 3, dt),
         "attn_fp8_quantize_qkv": (lambda: (binding.attn_fp8_quantize(q, True, seed, x8=q8, descale=dsq),
                                            binding.attn_fp8_quantize(k, True, seed, x8=k8, descale=dsk),
                                            binding.attn_fp8_quantize(v, False, seed, x8=v8, descale=dsv)),
@@ -112,6 +137,8 @@ def main():
                                                       o=o8, lse=lse8), F,
                          3 * elem + elem * 2 + B * H * N * 4 + 3 * B * H * nblk * 4, "fp8"),
     }
+    if args.forward_only:
+        comps = {f"attn_fwd_{dt}": comps[f"attn_fwd_{dt}"]}
     active = {}
     for name, c in comps.items():
         try:
@@ -120,7 +147,7 @@ def main():
             active[name] = c
         except binding.AttnError as e:
             print(f"# {name}: not built ({e})", file=sys.stderr)
-    if "attn_fwd_bf16" not in active:
+    if f"attn_fwd_{dt}" not in active:
         raise SystemExit("forward kernel failed")
 
     for _ in range(args.warmup):
@@ -165,7 +192,7 @@ def main():
     dom = max(comp_out, key=lambda n: comp_out[n]["ms"])
     fn, flops, nbytes, pk = active[dom]
     ms = comp_out[dom]["ms"]
-    traffic = stored_traffic(dom)
+    traffic = stored_traffic(dom) if default else None
     if flops:
         ach = flops / (ms * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_TFLOPS[pk],
@@ -178,15 +205,15 @@ def main():
     roof["algorithmic_bytes"] = nbytes
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if default and not args.no_cpu_baseline:
         cpu = cpu_baseline(x, w, args.cpu_heads, list(active), seed)
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOPs/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16+fp8e4m3" if "attn_fwd_fp8" in active else "bf16", "data": "synthetic",
-        "config": {"workload": "attention B=2 N=8192 H=16 d=128 non-causal: bf16 fwd + bwd, fp8 quantize + fwd",
+        "dtype": f"{dt}+fp8e4m3" if "attn_fwd_fp8" in active else dt, "data": "synthetic",
+        "config": {"workload": wname,
                    "batch": B, "seq_len": N, "heads": H, "head_dim": d, "causal": causal,
                    "parallelism": "single GPU", "step": list(active)},
         "components": comp_out,
@@ -212,7 +239,7 @@ def cpu_baseline(x, w, heads, active, seed):
     t0 = time.perf_counter()
     oracle.forward(sub["q"], sub["k"], sub["v"], w["causal"])
     flops += f1
-    if "attn_bwd_bf16" in active:
+    if any(n.startswith("attn_bwd_") for n in active):
         oracle.backward(sub["q"], sub["k"], sub["v"], sub["do"], w["causal"])
         flops += 2.5 * f1
     if "attn_fwd_fp8" in active:
