@@ -43,7 +43,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8, help="heads of the workload timed on the oracle")
-    ap.add_argument("--workload", default=None, help="a workloads.CONFIGS name instead of the default workload")
+    import workloads
+    ap.add_argument("--workload", default=None, choices=sorted(workloads.CONFIGS),
+                    help="a workloads.CONFIGS name instead of the default workload")
     ap.add_argument("--seq-len", type=int, default=None, help="override N of --workload")
     ap.add_argument("--forward-only", action="store_true", help="time attn_fwd alone")
     ap.add_argument("--copy-calibration", action="store_true",
