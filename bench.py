@@ -99,7 +99,8 @@ def main():
     else:
         c = workloads.CONFIGS[args.workload]
         w = dict(B=c["B"], N=c["N"], H=c["H"], d=c["d"], causal=c["causal"][0], dtype=c["dtype"], seed=c["seed"],
-                 input_scale=c.get("input_scale", 1.0))
+                 input_scale=c.get("input_scale", 1.0), outlier_frac=c.get("outlier_frac", 0.0),
+                 outlier_sigma=c.get("outlier_sigma", 10.0))
         wname = args.workload
     if args.seq_len is not None:
         w["N"] = args.seq_len
@@ -109,7 +110,8 @@ def main():
                  + (", forward only" if args.forward_only else ""))
     else:
         wname += ": bf16 fwd + bwd, fp8 quantize + fwd"
-    x = workloads.make_inputs(B, N, H, d, dt, w["seed"], w.get("input_scale", 1.0), with_do=True)
+    x = workloads.make_inputs(B, N, H, d, dt, w["seed"], w.get("input_scale", 1.0), w.get("outlier_frac", 0.0),
+                              w.get("outlier_sigma", 10.0), with_do=True)
     q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
     F = 4.0 * B * H * N * N * d * (0.5 if causal else 1.0)
     seed = 0x5EED
