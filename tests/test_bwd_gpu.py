@@ -84,7 +84,8 @@ def test_bwd_deterministic_and_workspace_checked(lib):
     assert e.value.status == 3
 
 
-FULL = [("c3_d128", True), ("c3_d256", True)]
+# the causal workloads, and the benchmark's non-causal B=2 N=8192 H=16 d=128 shape
+FULL = [("c3_d128", True), ("c3_d256", True), ("c2_8192_d128", False)]
 
 
 @pytest.mark.parametrize("name,causal", FULL, ids=[f[0] for f in FULL])
