@@ -1,4 +1,5 @@
-"""Compile the gfx950 HIP sources in csrc/ into the in-tree shared library libattn.so.
+"""Compile the gfx950 HIP sources in csrc/ into the in-tree shared library libattn.so, and
+the measurement probes in probe/ into libattn_probe.so (loaded by bench.py only).
 
 Every call recompiles (the object files are cheap to rebuild and this keeps the library in
 step with its sources). Used by ``__graft_entry__.build()`` and ``python -m
@@ -15,6 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libattn.so")
+PROBE_SRC = os.path.join(HERE, "probe", "attn_probe.hip")
+PROBE_LIB = os.path.join(HERE, "libattn_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -41,11 +44,15 @@ def build(verbose=False, jobs=None):
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     os.makedirs(OBJDIR, exist_ok=True)
     objs = [os.path.join(OBJDIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
-    jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
+    probe_obj = os.path.join(OBJDIR, "attn_probe.o")
+    jobs = jobs or min(len(srcs) + 1, os.cpu_count() or 4, 16)
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        outs = list(ex.map(lambda so: _run([HIPCC, *FLAGS, "-c", so[0], "-o", so[1]]), zip(srcs, objs)))
+        outs = list(ex.map(lambda so: _run([HIPCC, *FLAGS, "-c", so[0], "-o", so[1]]),
+                           zip(srcs + [PROBE_SRC], objs + [probe_obj])))
     tmp = LIB + ".tmp"
     outs.append(_run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]))
+    outs.append(_run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", probe_obj, "-o", PROBE_LIB + ".tmp"]))
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     # The host compilation pass can silently drop a kernel's launch stub (for instance when
     # substitution fails in device-only code); the library would then fail to load. Catch
     # that here rather than at first use.

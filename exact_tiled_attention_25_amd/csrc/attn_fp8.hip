@@ -223,6 +223,27 @@ template <int D> __host__ __device__ constexpr int f8_vpitch() { return D + 32; 
 __device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
+// The same with B multiplied by 2^(code_b - 127) (E8M0 scale code; A unscaled, code 127).
+__device__ __forceinline__ f32x16 mfma_f8_scaled(const i32x8& a, const i32x8& b, f32x16 c, int code_b) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, code_b);
+}
+
+// Row sums of the e4m3 P operand on the matrix core. The 32x32x64 P^T operand (lane l: query
+// l%32, keys of half l/32) read as the B operand of a 16x16x128 product has lane l in column
+// l%16 and K-chunk l/16, i.e. chunk c holds query 16*(c%2) + l%16. An A operand of ones on
+// the chunks of one parity per row picks one query per output row; choosing, for the rows
+// 4*(l/16) .. +3 that lane l receives, the parity of lane l's own query gives every lane the
+// sum of its query's 64 rounded operands (in all four result registers).
+__device__ __forceinline__ i32x8 rowsum_selector(int lane) {
+  const int m = lane & 15, c = lane >> 4;
+  const int one4 = 0x38383838;   // four e4m3 ones
+  const int v = ((c & 1) == ((m >> 2) & 1)) ? one4 : 0;
+  return i32x8{v, v, v, v, v, v, v, v};
+}
+__device__ __forceinline__ float rowsum_f8(const i32x8& sel, const i32x8& p) {
+  const f32x4 r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, p, f32x4{}, 0, 0, 0, 0, 0, 0);
+  return r[0];
+}
 
 // K operand of S^T = K Q^T: lane l holds key row kb*32 + l%32, dims 64*ks + 32*(l/32) .. +31.
 template <int P>
@@ -334,6 +355,8 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
   dvm = red[0];
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) dvm = fmaxf(dvm, red[w]);
+  // A head whose V descales are all zero has V = 0: any positive reference gives O = 0.
+  if (!(dvm > 0.f)) dvm = 1.0f;
 
   // Q^T operand: lane holds query q0 + l32, dims 64*ks + 32*hf .. +31.
   i32x8 qreg[NKS];
@@ -383,13 +406,21 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
   };
   float dk_c, dv_c;   // descales of the tile the next iteration exponentiates
   load_desc(0, dk_c, dv_c);
-  // The weight 64 * dv/dv_max of that tile's P~ enters the exp2 argument as its log2, and
-  // the row sum takes the unweighted P~ through its reciprocal; both are formed one tile
-  // ahead, off the path from the tile barrier to the first exponential.
+  // The weight 64 * dv/dv_max of a tile's P~ is split as 2^e * w, w in [32, 64): w enters the
+  // exp2 argument as its log2 (so every tile's e4m3 operand P~ w spans the same range, whatever
+  // its V scale), and 2^e is the E8M0 scale code 127 + e that the PV product applies to that
+  // operand exactly. The row sums take P~ and the rounded operands through 1/w. A V block
+  // with descale 0 (all zeros) gets w = 64 and code 0 (2^-127): its keys still count in both
+  // row sums, and its zero codes add nothing to O. Formed one tile ahead, off the path from
+  // the tile barrier to the first exponential.
   const float inv_dvm = 1.0f / dvm;
   float logw_c, rw_c;
+  int sc_c;
   auto set_weight = [&](float dv) {
-    const float w = kPScale * dv * inv_dvm;
+    const float r = dv * inv_dvm;   // in [0, 1]
+    const bool normal = r >= 0x1p-126f;
+    const float w = normal ? kPScale * __builtin_amdgcn_frexp_mantf(r) : kPScale;
+    sc_c = normal ? 127 + __builtin_amdgcn_frexp_expf(r) : 0;
     logw_c = fast_log2(w);
     rw_c = __builtin_amdgcn_rcpf(w);
   };
@@ -405,7 +436,11 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
   f32x16 oacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  // l_run: the row sum of the unrounded P~ (lane partial over its half of each tile), which
+  // gives L; l_rnd: the row sum of the e4m3-rounded operands divided by their weights, which
+  // normalises O, so that O's weights are exactly the operands the PV product used.
+  float m_run = -INFINITY, l_run = 0.f, l_rnd = 0.f;
+  const i32x8 sel = rowsum_selector(lane);
   const int k_lane = k8_lane_off<P8>(lane), v_lane = vt8_lane_off<PV8>(lane);
 
   wait_before(0);
@@ -464,6 +499,7 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
       const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_cand);
       m_run = m_cand;
       l_run *= alpha;
+      l_rnd *= alpha;
 #pragma unroll
       for (int i = 0; i < NDB; ++i)
 #pragma unroll
@@ -513,12 +549,13 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
     const float coef_n = cq * dk_n;
     i32x8 vop[S2];
     float mx = -INFINITY, psum = 0.f;
+    const float rsum = rowsum_f8(sel, pk);
 #pragma unroll
     for (int t = 0; t < PF && t < S2; ++t) vop[t] = lds_vt8<PV8>(vc, t);
 #pragma unroll
     for (int t = 0; t < S2; ++t) {
       if (t + PF < S2) vop[t + PF] = lds_vt8<PV8>(vc, t + PF);
-      oacc[t] = mfma_f8(vop[t], pk, oacc[t]);
+      oacc[t] = mfma_f8_scaled(vop[t], pk, oacc[t], sc_c);
 #pragma unroll
       for (int u = 0; u < MPS; u += 2) {
         const int i2 = MPS * t + u;
@@ -530,6 +567,7 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
       __builtin_amdgcn_sched_barrier(0);
     }
     l_run = fmaf(psum, rw_c, l_run);
+    l_rnd = fmaf(rsum, rw_c, l_rnd);
     mx = xhalf_max(mx);
     mx_next = mx * coef_n;
     coef_c = coef_n;
@@ -581,9 +619,10 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
           pk[4 * kb + r4] = (int)cvt4_fp8(e4[0], e4[1], e4[2], e4[3]);
         }
       l_run = fmaf(psum, rw_c, l_run);
+      l_rnd = fmaf(rowsum_f8(sel, pk), rw_c, l_rnd);
       const char* vc = vst(j) + v_lane;
 #pragma unroll
-      for (int i = 0; i < NDB; ++i) oacc[i] = mfma_f8(lds_vt8<PV8>(vc, i), pk, oacc[i]);
+      for (int i = 0; i < NDB; ++i) oacc[i] = mfma_f8_scaled(lds_vt8<PV8>(vc, i), pk, oacc[i], sc_c);
       if (j + 1 < nkt_w) {
         tile_scores(sc, kst(j + 1) + k_lane);
         if (is_edge(j + 1)) tile_mask(sc, (j + 1) * BC);
@@ -599,7 +638,7 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
 
   if (nkt_w > 0) {
     const float l_tot = xhalf_sum(l_run);
-    const float fac = dvm / kPScale / l_tot;
+    const float fac = dvm / kPScale / l_rnd;
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
     for (int i = 0; i < NDB; ++i)

@@ -179,7 +179,10 @@ attn_status_t attn_fp8_quantize_rope(const void* x, uint8_t* x8, float* descale,
  * rotation is orthogonal the scores do not depend on it, and `hadamard_seed` is carried
  * only to describe the inputs. The probabilities are rounded to e4m3 for the P V product,
  * scaled by 64 * dv/dv_max (dv the V descale of the key's block, dv_max the head's largest);
- * the epilogue undoes that factor exactly. O is written in `out_dtype`, LSE in fp32 (natural log). */
+ * the epilogue undoes that factor exactly. O is written in `out_dtype`, LSE in fp32 (natural log).
+ * Every descale must be finite and >= 0 (the quantisers write positive ones); a zero descale
+ * is a block of zeros, and a head whose V descales are all zero gets O = 0. Negative or
+ * non-finite descales give undefined results (no access leaves the tensors). */
 attn_status_t attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                            void* o, float* lse, int B, int H, int N, int d, int causal,
                            float scale, const float* descale_q, const float* descale_k,
