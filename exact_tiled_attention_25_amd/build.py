@@ -46,8 +46,12 @@ def build(verbose=False, jobs=None):
     objs = [os.path.join(OBJDIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
     probe_obj = os.path.join(OBJDIR, "attn_probe.o")
     jobs = jobs or min(len(srcs) + 1, os.cpu_count() or 4, 16)
+    def flags(src):
+        # the C ABI's argument checks must see NaN arguments (-fno-honor-nans would let the
+        # compiler assume a float argument is never NaN); it holds no kernels
+        return [f for f in FLAGS if f != "-fno-honor-nans"] if src.endswith("attn_api.hip") else FLAGS
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        outs = list(ex.map(lambda so: _run([HIPCC, *FLAGS, "-c", so[0], "-o", so[1]]),
+        outs = list(ex.map(lambda so: _run([HIPCC, *flags(so[0]), "-c", so[0], "-o", so[1]]),
                            zip(srcs + [PROBE_SRC], objs + [probe_obj])))
     tmp = LIB + ".tmp"
     outs.append(_run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]))

@@ -42,6 +42,7 @@ attn_status_t check_sizes(int B, int H, int N, int d, bool* empty) {
   return ATTN_OK;
 }
 
+// (This file is built with NaNs honoured, unlike the kernels: see build.py.)
 bool bad_scale(float scale) { return !std::isfinite(scale) || scale < 0.f; }
 
 attn_status_t launched(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ELAUNCH; }

@@ -91,3 +91,15 @@ def test_null_pointers_rejected(lib):
     assert lib.attn_fp8_quantize_per_tensor(None, None, None, 1, 1, 16, 100, 0, 1, 0, None) == 2
     assert lib.attn_fwd_fp8(None, None, None, None, None, 1, 1, 16, 64, 0, 0.125, None, None, None, 0, 0,
                             None) == 1
+
+
+def test_non_finite_scale_rejected_with_pointers(lib):
+    """NaN and infinite scales are rejected even when every pointer is set (the checks are not
+    masked by the null-pointer check, and the compiler may not assume arguments are NaN-free)."""
+    fake = [ctypes.c_void_p(4096)] * 9
+    for bad in (float("nan"), float("inf"), -1.0):
+        assert lib.attn_fwd(*fake[:5], 1, 1, 16, 64, 0, bad, 0, None) == 1
+        assert lib.attn_bwd(*fake, 1, 1, 16, 64, 0, bad, 0, None, 0, None) == 1
+        assert lib.attn_fwd_fp8(*fake[:5], 1, 1, 16, 64, 0, bad, *fake[:3], 0, 0, None) == 1
+    for base in (float("nan"), float("inf")):
+        assert lib.attn_fp8_quantize_rope(*fake[:3], 1, 1, 16, 64, 0, base, 1, 0, None) == 1
