@@ -22,7 +22,8 @@ FP8_BLOCK = 64
 EXPORTS = ("attn_fwd", "attn_fwd_gqa", "attn_fwd_varlen", "attn_fwd_splitkv_workspace_bytes",
            "attn_fwd_splitkv", "attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_gqa",
            "attn_bwd_varlen_workspace_bytes", "attn_bwd_varlen", "attn_fp8_quantize",
-           "attn_fp8_quantize_per_tensor", "attn_fp8_quantize_rope", "attn_fwd_fp8", "attn_strerror")
+           "attn_fp8_quantize_per_tensor", "attn_fp8_quantize_rope", "attn_fwd_fp8", "attn_strerror",
+           "attn_bwd_noalloc_max_rows", "attn_bwd_noalloc")
 _DTYPE_CODE = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_FP16}
 
 _lib = None
@@ -62,6 +63,10 @@ def load(path=None):
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     L.attn_bwd.restype = i
+    L.attn_bwd_noalloc_max_rows.argtypes = []
+    L.attn_bwd_noalloc_max_rows.restype = sz
+    L.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    L.attn_bwd_noalloc.restype = i
     L.attn_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
     L.attn_bwd_gqa.restype = i
     for fn in (L.attn_fp8_quantize, L.attn_fp8_quantize_per_tensor):
@@ -276,6 +281,28 @@ def attn_bwd(q, k, v, o, lse, do, causal=False, scale=None, dq=None, dk=None, dv
                                        _default_scale(d, scale), _DTYPE_CODE[q.dtype], _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _stream(q, stream)))
     return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, do, causal=False, scale=None, dq=None, dk=None, dv=None, stream=None):
+    """attn_bwd without a workspace: the library's fixed device scratch holds D (B*H*N rows at
+    most attn_bwd_noalloc_max_rows()). Allocates nothing when dq, dk, dv are given."""
+    _tensor(q, "q", dtypes=tuple(_DTYPE_CODE))
+    B, N, H, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+        _tensor(t, name, q.shape, (q.dtype,), q.device)
+    _tensor(lse, "lse", (B, H, N), (torch.float32,), q.device)
+    dq = torch.empty_like(q) if dq is None else _tensor(dq, "dq", q.shape, (q.dtype,), q.device)
+    dk = torch.empty_like(q) if dk is None else _tensor(dk, "dk", q.shape, (q.dtype,), q.device)
+    dv = torch.empty_like(q) if dv is None else _tensor(dv, "dv", q.shape, (q.dtype,), q.device)
+    _check("attn_bwd_noalloc", load().attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                                                       _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, int(bool(causal)),
+                                                       _default_scale(d, scale), _DTYPE_CODE[q.dtype],
+                                                       _stream(q, stream)))
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc_max_rows():
+    return int(load().attn_bwd_noalloc_max_rows())
 
 
 def attn_fp8_quantize(x, rotate, hadamard_seed=0, x8=None, descale=None, stream=None, per_tensor=False):

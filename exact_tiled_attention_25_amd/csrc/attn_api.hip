@@ -29,6 +29,29 @@ attn_status_t check_device() {
 
 bool supported_d(int d) { return d == 64 || d == 128 || d == 256; }
 
+// Fixed device scratch of the no-allocation backward: D = rowsum(dO o O), one fp32 per
+// (batch, head, row). In host code `scratch` only names the symbol; its device address on
+// each GPU comes from hipGetSymbolAddress (each device holds its own copy until the process
+// ends).
+constexpr size_t kNoAllocMaxRows = (size_t)1 << 22;   // 16 MiB
+__device__ __align__(256) float scratch[kNoAllocMaxRows];
+std::atomic<float*> g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up on the first call there.
+attn_status_t scratch_address(float** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_EDEVICE;
+  float* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return ATTN_ELAUNCH;
+    p = (float*)q;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return ATTN_OK;
+}
+
 // Sizes shared by every entry point. Byte offsets inside one batch slice are 32-bit
 // (buffer addressing), so a batch slice of a 16-bit tensor must stay below 2^31 bytes.
 attn_status_t check_sizes(int B, int H, int N, int d, bool* empty) {
@@ -199,6 +222,27 @@ attn_status_t attn_bwd_varlen(const void* q, const void* k, const void* v, const
                     workspace, workspace_bytes, stream, cu_seqlens, T);
 }
 
+size_t attn_bwd_noalloc_max_rows(void) { return kNoAllocMaxRows; }
+
+attn_status_t attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                               int B, int H, int N, int d, int causal, float scale,
+                               attn_dtype_t dtype, attn_stream_t stream) {
+  // the argument checks of attn_bwd, then the size limit, then the device and its scratch
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_EINVAL;
+  if (bad_scale(scale)) return ATTN_EINVAL;
+  bool empty = false;
+  attn_status_t st = check_sizes(B, H, N, d, &empty);
+  if (st != ATTN_OK || empty) return st;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_EINVAL;
+  if ((double)B * H * N > (double)kNoAllocMaxRows) return ATTN_ETOOLARGE;
+  if ((st = check_device()) != ATTN_OK) return st;
+  float* ws = nullptr;
+  if ((st = scratch_address(&ws)) != ATTN_OK) return st;
+  return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, B, H, H, N, d, causal, scale, dtype, ws,
+                    kNoAllocMaxRows * sizeof(float), stream);
+}
+
 attn_status_t attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
                            int B, int H, int H_kv, int N, int d, int causal, float scale,
@@ -277,6 +321,7 @@ const char* attn_strerror(attn_status_t s) {
     case ATTN_EWORKSPACE: return "workspace missing or too small (see attn_*_workspace_bytes)";
     case ATTN_ELAUNCH: return "kernel launch failed";
     case ATTN_EDEVICE: return "current device is not an MI355X-class gfx950 GPU";
+    case ATTN_ETOOLARGE: return "problem larger than the fixed scratch of a no-allocation entry point";
   }
   return "unknown status";
 }

@@ -41,7 +41,8 @@ typedef enum {
   ATTN_EUNSUPPORTED = 2,  /* d not in {64,128,256}, or a size whose indices overflow 32 bits */
   ATTN_EWORKSPACE = 3,    /* workspace missing or smaller than attn_bwd_workspace_bytes() */
   ATTN_ELAUNCH = 4,       /* the HIP runtime rejected a kernel launch */
-  ATTN_EDEVICE = 5        /* the current device is not gfx950 */
+  ATTN_EDEVICE = 5,       /* the current device is not gfx950 */
+  ATTN_ETOOLARGE = 6      /* beyond the fixed scratch of attn_bwd_noalloc */
 } attn_status_t;
 
 /* A hipStream_t passed as an opaque pointer; NULL means the null stream. */
@@ -121,6 +122,22 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
                        int B, int H, int N, int d, int causal, float scale,
                        attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
                        attn_stream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): attn_bwd with no workspace argument.
+ * Same arguments, kernels, results (bit for bit) and errors as attn_bwd; the per-row
+ * statistic D lives in a fixed library-owned device array of attn_bwd_noalloc_max_rows()
+ * fp32 entries (4 Mi rows, 16 MiB, held by each GPU the library runs on until the process
+ * ends). B*H*N above that limit returns ATTN_ETOOLARGE. Nothing is allocated, also not on
+ * the first call on a device (which looks up the array's device address). Every call on
+ * one GPU shares that array: calls that may overlap on the same GPU (different streams,
+ * host threads) race and must be ordered by the caller. ATTN_ELAUNCH if the array's device
+ * address cannot be obtained. */
+size_t attn_bwd_noalloc_max_rows(void);
+attn_status_t attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                               int B, int H, int N, int d, int causal, float scale,
+                               attn_dtype_t dtype, attn_stream_t stream);
 
 /* Grouped-query backward: shapes as attn_fwd_gqa; dq [B][N][H][d], dk and dv
  * [B][N][H_kv][d]. A key/value head's dK and dV are the sums of the gradients through each of

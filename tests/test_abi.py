@@ -28,9 +28,9 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_strerror_covers_every_status(lib):
-    msgs = {s: lib.attn_strerror(s).decode() for s in range(6)}
+    msgs = {s: lib.attn_strerror(s).decode() for s in range(7)}
     assert msgs[0] == "success"
-    assert len(set(msgs.values())) == 6
+    assert len(set(msgs.values())) == 7
     assert lib.attn_strerror(99).decode() == "unknown status"
 
 
@@ -93,6 +93,19 @@ def test_null_pointers_rejected(lib):
                             None) == 1
 
 
+def test_bwd_noalloc_limits_without_device(lib):
+    """The no-allocation backward checks its arguments like attn_bwd, then its fixed scratch
+    limit (B*H*N rows), all before any device access."""
+    assert lib.attn_bwd_noalloc_max_rows() == 1 << 22
+    nul = [None] * 9
+    assert lib.attn_bwd_noalloc(*nul, 1, 1, 16, 64, 0, 0.125, 0, None) == 1
+    assert lib.attn_bwd_noalloc(*nul, 0, 1, 16, 64, 0, 0.125, 0, None) == 0
+    assert lib.attn_bwd_noalloc(*nul, 1, 1, 16, 96, 0, 0.125, 0, None) == 2
+    fake = [ctypes.c_void_p(4096)] * 9   # never dereferenced: the size check fails first
+    assert lib.attn_bwd_noalloc(*fake, 2, 16, (1 << 17) + 1, 64, 0, 0.125, 0, None) == 6
+    assert lib.attn_bwd_noalloc(*fake, 1, 1, 16, 64, 0, float("nan"), 0, None) == 1
+
+
 def test_non_finite_scale_rejected_with_pointers(lib):
     """NaN and infinite scales are rejected even when every pointer is set (the checks are not
     masked by the null-pointer check, and the compiler may not assume arguments are NaN-free)."""
@@ -100,6 +113,7 @@ def test_non_finite_scale_rejected_with_pointers(lib):
     for bad in (float("nan"), float("inf"), -1.0):
         assert lib.attn_fwd(*fake[:5], 1, 1, 16, 64, 0, bad, 0, None) == 1
         assert lib.attn_bwd(*fake, 1, 1, 16, 64, 0, bad, 0, None, 0, None) == 1
+        assert lib.attn_bwd_noalloc(*fake, 1, 1, 16, 64, 0, bad, 0, None) == 1
         assert lib.attn_fwd_fp8(*fake[:5], 1, 1, 16, 64, 0, bad, *fake[:3], 0, 0, None) == 1
     for base in (float("nan"), float("inf")):
         assert lib.attn_fp8_quantize_rope(*fake[:3], 1, 1, 16, 64, 0, base, 1, 0, None) == 1
