@@ -192,7 +192,9 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
     }
   };
   auto fetch_into = [&](Pos ps, char* st) {
-    const int qt = ps.qt, hq = kvh * G + ps.g;
+    // the tile position is the same in every lane; the compiler cannot tell through the
+    // loop-carried position (it would wrap each DMA instruction in a loop over lanes)
+    const int qt = (int)uniform((uint32_t)ps.qt), hq = kvh * G + (int)uniform((uint32_t)ps.g);
     if (tid < BQ) {
       const bool in = qt * BQ + tid < N;
       ((float*)(st + OFF_L))[tid] = in ? lraw * kLog2e : INFINITY;   // P = exp2(s*c - inf) = 0 past the end
@@ -449,6 +451,10 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(BwdParams p)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = tid >> 6;
+  // the DMA's LDS base depends on the wave index: give it a provably uniform copy (with the
+  // plain index the compiler wraps each DMA instruction in a loop over lanes; making the
+  // wave index itself scalar everywhere changes the register allocation and spills)
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const int H = p.H;
   const int nqt = (p.N + BR - 1) / BR;   // p.N: the (longest) sequence length
@@ -484,8 +490,8 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(BwdParams p)
   dma_init<KPlan, kWaves, SWZ>(kvoff, kv_row_bytes, wave, lane);
   dma_init<VPlan, kWaves>(vvoff, kv_row_bytes, wave, lane);
   auto fetch_into = [&](int j, char* st) {
-    dma_issue<KPlan, kWaves>(kvoff, st, kbase, j * BC, kv_row_bytes, kv_nrec, wave);
-    dma_issue<VPlan, kWaves>(vvoff, st + KB, vbase, j * BC, kv_row_bytes, kv_nrec, wave);
+    dma_issue<KPlan, kWaves>(kvoff, st, kbase, j * BC, kv_row_bytes, kv_nrec, wave_u);
+    dma_issue<VPlan, kWaves>(vvoff, st + KB, vbase, j * BC, kv_row_bytes, kv_nrec, wave_u);
   };
   fetch_into(0, smem);
 

@@ -81,6 +81,13 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// A 32-bit value the caller knows to be the same in every lane, made provably wave-uniform
+// (scalar): buffer resources and the LDS base of a DMA must live in scalar registers, and
+// where the compiler cannot prove uniformity it wraps each such instruction in a loop over
+// lanes. (Only for values the compiler cannot see are uniform: forcing an already scalar
+// value through readfirstlane can leave a vector copy that other users then pick up.)
+__device__ __forceinline__ uint32_t uniform(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -79,7 +79,9 @@ __device__ __forceinline__ void dma_init(uint32_t* voff, uint32_t row_bytes, int
 // DMA of the tile whose first row is `row0` of the (batch, head) view starting at
 // `head_base` (`nrec` bytes valid from there). The buffer resource is built here: a
 // resource passed into a function template fails substitution in the host compilation
-// pass, which silently drops the kernel's launch stub.
+// pass, which silently drops the kernel's launch stub. Every argument must be provably
+// wave-uniform (the resource and the LDS base live in scalar registers); otherwise the
+// compiler wraps each load in a loop over the lanes' distinct values.
 template <class Plan, int NWAVES>
 __device__ __forceinline__ void dma_issue(const uint32_t* voff, char* dst, const char* head_base,
                                           int row0, uint32_t row_bytes, uint32_t nrec, int wave) {

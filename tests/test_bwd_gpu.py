@@ -99,3 +99,16 @@ def test_bwd_full_size_two_heads(lib, name, causal):
     for b, h in ((0, 0), (B - 1, H - 1)):
         ref = oracle.head_backward(x["q"][b, :, h], x["k"][b, :, h], x["v"][b, :, h], x["do"][b, :, h], causal)
         _check((dq[b, :, h], dk[b, :, h], dv[b, :, h]), ref, f"{name} b={b} h={h}")
+
+
+@pytest.mark.parametrize("dtype,causal", [("bf16", True), ("fp16", False)], ids=["bf16-causal", "fp16-full"])
+def test_bwd_ragged_default_form_one_head(lib, dtype, causal):
+    """Ragged N = 8000 at the benchmark's head count, in the launch configuration of the
+    full-size runs; one whole head against the oracle."""
+    B, N, H, d = 2, 8000, 16, 128
+    log(f"bwd ragged B={B} N={N} H={H} d={d} {dtype} causal={causal}")
+    x = workloads.make_inputs(B, N, H, d, dtype, 34, with_do=True)
+    dq, dk, dv = _gpu_bwd(x, causal)
+    b, h = 1, 9
+    ref = oracle.head_backward(x["q"][b, :, h], x["k"][b, :, h], x["v"][b, :, h], x["do"][b, :, h], causal)
+    _check((dq[b, :, h], dk[b, :, h], dv[b, :, h]), ref, f"ragged b={b} h={h}")

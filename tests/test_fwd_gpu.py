@@ -177,3 +177,58 @@ def test_fwd_full_size_sampled_rows(lib, name, causal):
     log(f"  max|dO|={worst_o:.3e} max|dL|={worst_l:.3e} relRMSE(O)={e['rel_rmse']:.3e}")
     assert worst_o <= 1e-2 and worst_l <= 1e-3 and e["rel_rmse"] <= 1e-2
     assert np.isfinite(o).all() and np.isfinite(lse).all()
+
+
+# Ragged N in the default (8-wave, ping-pong) form: N = 8000 is not a multiple of any tile,
+# and B*H*ceil(N/256) >= 256 workgroups keeps the default form selected; bf16 and fp16, with
+# and without the causal mask. The short-grid form covers the small cases above.
+RAGGED = [(dt, c) for dt in ("bf16", "fp16") for c in (False, True)]
+
+
+@pytest.mark.parametrize("dtype,causal", RAGGED, ids=[f"{d}-{'causal' if c else 'full'}" for d, c in RAGGED])
+def test_fwd_ragged_default_form_sampled_rows(lib, dtype, causal):
+    B, N, H, d = 2, 8000, 16, 128
+    log(f"fwd ragged default form B={B} N={N} H={H} d={d} {dtype} causal={causal}")
+    x = workloads.make_inputs(B, N, H, d, dtype, 24)
+    from exact_tiled_attention_25_amd import binding
+    o, lse = binding.attn_fwd(x["q"].cuda(), x["k"].cuda(), x["v"].cuda(), causal=causal)
+    o, lse = to64(o), to64(lse)
+    rng = np.random.default_rng(24)
+    got, ref, worst_l = [], [], 0.0
+    for b, h in ((0, 0), (1, 15), (1, 3)):
+        # the last, partly filled query tile (rows 7936..7999) and its last 32-row wave, and
+        # rows throughout
+        rows = np.unique(np.concatenate([_sampled_rows(rng, N, 64), np.arange(7936, 8000, 7), [7999]]))
+        o_ref, l_ref = oracle.forward_rows(x["q"], x["k"], x["v"], b, h, rows, causal)
+        got.append(o[b, rows, h]); ref.append(o_ref)
+        worst_l = max(worst_l, np.abs(lse[b, h, rows] - l_ref).max())
+    e = errs(np.concatenate(got), np.concatenate(ref))
+    log(f"  max|dO|={e['max_abs']:.3e} max|dL|={worst_l:.3e} relRMSE(O)={e['rel_rmse']:.3e}")
+    assert e["max_abs"] <= 1e-2 and worst_l <= 1e-3 and e["rel_rmse"] <= 1e-2
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+
+
+# The long-context sweep (fp16, inputs x0.5, causal, B=1, H=16, d=128) at every length the
+# benchmark times, through attn_fwd: N = 1K and 2K take the short-grid form, longer N the
+# default one.
+SWEEP = [1024, 2048, 4096, 8192, 16384]
+
+
+@pytest.mark.parametrize("N", SWEEP)
+def test_fwd_long_context_sweep_sampled_rows(lib, N):
+    B, H, d = 1, 16, 128
+    log(f"fwd sweep fp16 causal B={B} N={N} H={H} d={d}")
+    x = workloads.make_inputs(B, N, H, d, "fp16", 4, input_scale=0.5)
+    from exact_tiled_attention_25_amd import binding
+    o, lse = binding.attn_fwd(x["q"].cuda(), x["k"].cuda(), x["v"].cuda(), causal=True)
+    o, lse = to64(o), to64(lse)
+    rng = np.random.default_rng(N)
+    got, ref, worst_l = [], [], 0.0
+    for h in (0, 7, 15):
+        rows = _sampled_rows(rng, N, 64)
+        o_ref, l_ref = oracle.forward_rows(x["q"], x["k"], x["v"], 0, h, rows, True)
+        got.append(o[0, rows, h]); ref.append(o_ref)
+        worst_l = max(worst_l, np.abs(lse[0, h, rows] - l_ref).max())
+    e = errs(np.concatenate(got), np.concatenate(ref))
+    log(f"  max|dO|={e['max_abs']:.3e} max|dL|={worst_l:.3e} relRMSE(O)={e['rel_rmse']:.3e}")
+    assert e["max_abs"] <= 1e-2 and worst_l <= 1e-3 and e["rel_rmse"] <= 1e-2
