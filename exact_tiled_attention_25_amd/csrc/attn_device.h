@@ -89,6 +89,11 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 __device__ __forceinline__ uint32_t uniform(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// max(max(a, b), c): a running maximum written this way (two new values per step) folds
+// into one v_max3_f32 per step; max(a, max(b, c)) pairs the new values first and costs more.
+// (Not inline asm: the compiler inserts the wait states that a read or write next to an
+// in-flight MFMA needs only for instructions it emits itself.)
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // Workgroups are handed to the 8 XCDs round-robin (block b runs on XCD b % 8). Give each XCD

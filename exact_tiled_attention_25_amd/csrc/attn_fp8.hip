@@ -508,9 +508,10 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
   };
 
   // Interior tiles, pipelined with the instruction order written out. Block 1: one S(j+1)
-  // MFMA per step, EPS exponentials of tile j under each, packed to fp8 four at a time.
-  // Block 2: one P~(j)V(j) MFMA per step (one per 32-dim output block), the row-sum terms
-  // of tile j and the row maximum of tile j+1 under it.
+  // MFMA per step, EPS exponentials of tile j under each, packed to fp8 four at a time and
+  // added to the row sum (two partial sums) as they come, so that the fp32 P~ values do not
+  // stay live into block 2. Block 2: one P~(j)V(j) MFMA per step (one per 32-dim output
+  // block), the rounded operands' row sum, and the row maximum of tile j+1 under it.
   constexpr int S1 = NKB * NKS;
   constexpr int S2 = NDB;
   constexpr int EPS = 16 * NKB / S1;
@@ -528,6 +529,7 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
     i32x8 pk;
     i32x8 kop[S1];
     float e[16 * NKB];
+    float psum_a = 0.f, psum_b = 0.f;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < PF && t < S1; ++t) kop[t] = lds_k8<P8>(kn, t % NKB, t / NKB);
@@ -541,7 +543,10 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
         const int i = EPS * t + u;
         e[i] = fast_exp2(fmaf(cur[i >> 4][i & 15], coef_c, bias));
         if ((i & 3) == 3) pk[i >> 2] = (int)cvt4_fp8(e[i - 3], e[i - 2], e[i - 1], e[i]);
+        if (i & 1) psum_b += e[i]; else psum_a += e[i];
       }
+      pin(psum_a);
+      pin(psum_b);
       __builtin_amdgcn_sched_barrier(0);
     }
     // late waves: the barrier that ends this tile comes between the two blocks
@@ -559,14 +564,11 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
 #pragma unroll
       for (int u = 0; u < MPS; u += 2) {
         const int i2 = MPS * t + u;
-        psum += e[i2];
-        psum += e[i2 + 1];
-        mx = fmaxf(mx, fmaxf(nxt[i2 >> 4][i2 & 15], nxt[(i2 + 1) >> 4][(i2 + 1) & 15]));
+        mx = max3(mx, nxt[i2 >> 4][i2 & 15], nxt[(i2 + 1) >> 4][(i2 + 1) & 15]);
       }
-      pin(psum);
       __builtin_amdgcn_sched_barrier(0);
     }
-    l_run = fmaf(psum, rw_c, l_run);
+    l_run = fmaf(psum_a + psum_b, rw_c, l_run);
     l_rnd = fmaf(rsum, rw_c, l_rnd);
     mx = xhalf_max(mx);
     mx_next = mx * coef_n;

@@ -376,7 +376,7 @@ __global__ __launch_bounds__((fwd_threads<D, SMALL>()), (fwd_wgs<D, SMALL>())) v
           const int i2 = MPS * t + u;
           psum += e[i2];
           psum += e[i2 + 1];
-          mx = fmaxf(mx, fmaxf(nxt[i2 >> 4][i2 & 15], nxt[(i2 + 1) >> 4][(i2 + 1) & 15]));
+          mx = max3(mx, nxt[i2 >> 4][i2 & 15], nxt[(i2 + 1) >> 4][(i2 + 1) & 15]);
         }
       }
       pin(psum);   // keep the sum's adds in this step (the compiler would sink them)
