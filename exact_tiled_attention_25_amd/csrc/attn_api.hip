@@ -29,12 +29,13 @@ attn_status_t check_device() {
 
 bool supported_d(int d) { return d == 64 || d == 128 || d == 256; }
 
-// Fixed device scratch of the no-allocation backward: D = rowsum(dO o O), one fp32 per
-// (batch, head, row). In host code `scratch` only names the symbol; its device address on
-// each GPU comes from hipGetSymbolAddress (each device holds its own copy until the process
-// ends).
-constexpr size_t kNoAllocMaxRows = (size_t)1 << 22;   // 16 MiB
-__device__ __align__(256) float scratch[kNoAllocMaxRows];
+// Fixed device scratch of the no-allocation backward: the backward's per-row statistics
+// (L log2 e, D = rowsum(dO o O)), two fp32 per (batch, head, row). In host code `scratch`
+// only names the symbol; its device address on each GPU comes from hipGetSymbolAddress
+// (each device holds its own copy until the process ends).
+constexpr size_t kNoAllocMaxRows = (size_t)1 << 22;
+constexpr size_t kBwdStatBytes = 2 * sizeof(float);   // workspace bytes per (batch, head, row)
+__device__ __align__(256) float scratch[2 * kNoAllocMaxRows];   // 32 MiB
 std::atomic<float*> g_scratch[kMaxDevices];
 
 // Device address of `scratch` on the current device, looked up on the first call there.
@@ -169,7 +170,7 @@ attn_status_t attn_fwd_splitkv(const void* q, const void* k, const void* v, void
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d) {
   (void)d;
   if (B <= 0 || H <= 0 || N <= 0) return 0;
-  return (size_t)B * H * N * sizeof(float);
+  return (size_t)B * H * N * kBwdStatBytes;
 }
 
 static attn_status_t bwd_common(const void* q, const void* k, const void* v, const void* o,
@@ -205,7 +206,7 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
 
 size_t attn_bwd_varlen_workspace_bytes(int T, int H) {
   if (T <= 0 || H <= 0) return 0;
-  return (size_t)T * H * sizeof(float);
+  return (size_t)T * H * kBwdStatBytes;
 }
 
 attn_status_t attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
@@ -240,7 +241,7 @@ attn_status_t attn_bwd_noalloc(const void* q, const void* k, const void* v, cons
   float* ws = nullptr;
   if ((st = scratch_address(&ws)) != ATTN_OK) return st;
   return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, B, H, H, N, d, causal, scale, dtype, ws,
-                    kNoAllocMaxRows * sizeof(float), stream);
+                    kNoAllocMaxRows * kBwdStatBytes, stream);
 }
 
 attn_status_t attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o,

@@ -8,12 +8,14 @@
 //   D_i = sum_t dO_it O_it (= sum_j P_ij dP_ij),  dK = scale dS^T Q,  dQ = scale dS K.
 //
 // gfx950 design. Three kernels on the caller's stream, no atomics (deterministic):
-//  1. bwd_pre:  D = rowsum(dO o O) in fp32 into the workspace (HBM-bound, one pass).
+//  1. bwd_pre:  D = rowsum(dO o O) in fp32 into the workspace, next to L log2 e (HBM-bound,
+//     one pass): the pair of a row is one 8-byte word, so the kernels below take a tile's
+//     L and D in one piece.
 //  2. bwd_dkdv: one workgroup per 128 keys of a key/value head (4 waves x 32 keys); with
 //     grouped key/value heads it visits the Q tiles of every query head of the group, so
 //     dK and dV are summed in registers (no atomics). Each wave keeps
 //     its keys' K and V in registers as MFMA B operands and its dK^T, dV^T accumulators in
-//     registers; Q and dO tiles stream through a two-stage LDS ring in both row-major (for
+//     registers; Q and dO tiles stream through a three-stage LDS ring in both row-major (for
 //     S = Q K^T and dP = dO V^T) and transposed (for dV^T += dO^T P, dK^T += Q^T dS) form.
 //     S and dP come out with one key per lane, so P and dS feed the next products straight
 //     from the accumulators (rows reordered by swap23, matched by the transposed tiles).
@@ -72,21 +74,24 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   if (row < nrows && tid % TPR == 0) {
     const int h = (int)(row % p.H);
     const long bn = row / p.H;
+    long i;
     if (p.cu) {
-      p.delta[(long)h * p.T + bn] = acc;
+      i = (long)h * p.T + bn;
     } else {
       const int n = (int)(bn % p.N), b = (int)(bn / p.N);
-      p.delta[((long)b * p.H + h) * p.N + n] = acc;
+      i = ((long)b * p.H + h) * p.N + n;
     }
+    ((float2*)p.stats)[i] = float2{p.lse[i] * kLog2e, acc};
   }
 }
 
 // ---------------------------------------------------------------- dK, dV
 // KV-outer: 4 waves x 32 keys per workgroup. Each wave keeps its keys' K and V as MFMA B
 // operands in registers and its dK^T, dV^T accumulators in registers. Q and dO tiles of BQ
-// queries arrive by DMA in a two-stage LDS ring (pitch 2d+48: read as rows for S = Q K^T
-// and dP = dO V^T, read transposed for dV^T += dO^T P and dK^T += Q^T dS), with the
-// tile's L (log2 domain) and D staged beside them. S and dP put one key per lane, so P and
+// queries and the tile's (L log2 e, D) pairs arrive by DMA in a three-stage LDS ring (read
+// as rows for S = Q K^T and dP = dO V^T, read transposed for dV^T += dO^T P and dK^T +=
+// Q^T dS). A tile's DMA is issued two tiles ahead of its use: one tile of MFMA work
+// (about 1 us) does not cover an HBM round trip under load. S and dP put one key per lane, so P and
 // dS feed the next products straight from the accumulators. The 64-query tile is worked
 // in two 32-query halves so that the VALU work of one half runs under the other's MFMAs:
 // scores(0) | scores(1) + softmax(0) | update(0) + softmax(1) | update(1).
@@ -128,9 +133,13 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
   constexpr int QP = SWZ ? 2 * D : rt_pitch<D>();
   using QPlan = DmaPlan<D, BQ, QP, kWaves>;
   constexpr int TB = QPlan::BYTES;
-  constexpr int OFF_DO = TB, OFF_L = 2 * TB, OFF_D = 2 * TB + BQ * 4;
-  constexpr int STAGE = 2 * TB + 2 * BQ * 4;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  // Stage: Q tile, dO tile, then one 256-byte slot per wave for the (L log2 e, D) pairs of
+  // tile rows 16w .. 16w+15 (first half; the second half takes the DMA's idle lanes).
+  constexpr int NSTAGE = 3;
+  constexpr int OFF_DO = TB, OFF_LD = 2 * TB;
+  constexpr int STAGE = 2 * TB + kWaves * 256;
+  static_assert(16 * kWaves >= BQ, "one L/D slot per 16 rows");
+  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps loop control scalar
@@ -178,39 +187,26 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
   };
   uint32_t qvoff[QPlan::NPW];
   dma_init<QPlan, kWaves, SWZ>(qvoff, row_bytes, wave, lane);
-  // L and D of query row (tile start + tid), tid < BQ: loaded one tile before they are staged
-  // into LDS, and used (scaled, masked past the end) only then. Any arithmetic on them at
-  // the load would make the wave wait there for the load and for the tile DMA issued just
-  // before it (the counter is in order).
-  float lraw = 0.f, draw = 0.f;
-  auto load_ld = [&](Pos ps) {
-    if (tid < BQ) {
-      const size_t lh = stat_row(p.cu, p.T, b, H, kvh * G + ps.g, sv);
-      const int q = min(ps.qt * BQ + tid, N - 1);   // in bounds; rows past the end are masked when staged
-      lraw = p.lse[lh + q];
-      draw = p.delta[lh + q];
-    }
-  };
+  // L/D DMA (4 bytes a lane): wave w brings the 32 words of rows 16w .. 16w+15 with lanes
+  // 0-31; lanes 32-63, and rows past the tile, are pointed past the buffer's end.
+  const uint32_t ld_voff = (lane < 32 && 16 * wave < BQ) ? (uint32_t)(32 * wave + lane) * 4 : 0x80000000u;
+  // DMA instructions this wave issues per tile (Q, dO, L/D), and the most of any wave
+  const int dma_per_tile = 2 * dma_count<QPlan, kWaves>(wave) + 1;
+  constexpr int MAX_PER_TILE = 2 * QPlan::NPW + 1;
   auto fetch_into = [&](Pos ps, char* st) {
     // the tile position is the same in every lane; the compiler cannot tell through the
     // loop-carried position (it would wrap each DMA instruction in a loop over lanes)
     const int qt = (int)uniform((uint32_t)ps.qt), hq = kvh * G + (int)uniform((uint32_t)ps.g);
-    if (tid < BQ) {
-      const bool in = qt * BQ + tid < N;
-      ((float*)(st + OFF_L))[tid] = in ? lraw * kLog2e : INFINITY;   // P = exp2(s*c - inf) = 0 past the end
-      ((float*)(st + OFF_D))[tid] = in ? draw : 0.f;
-    }
     const size_t qh_off = ((size_t)sv.start * H + hq) * D * 2;
     const uint32_t q_nrec = (uint32_t)N * row_bytes - (uint32_t)hq * D * 2;
     dma_issue<QPlan, kWaves>(qvoff, st, (const char*)p.q + qh_off, qt * BQ, row_bytes, q_nrec, wave);
     dma_issue<QPlan, kWaves>(qvoff, st + OFF_DO, (const char*)p.dout + qh_off, qt * BQ, row_bytes, q_nrec, wave);
+    // Rows past the end arrive as zeros: L = D = 0 there, and with their Q and dO rows zero
+    // too, P = 1 multiplies zeros (no contribution to dK or dV).
+    const size_t lrow = stat_row(p.cu, p.T, b, H, hq, sv) + (size_t)qt * BQ;
+    const auto rl = make_rsrc(p.stats + 2 * lrow, (uint32_t)(N - qt * BQ) * 8);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)(st + OFF_LD + wave * 256), 4, ld_voff, 0, 0, 0);
   };
-  Pos pos0 = first_pos(), pos1 = next_pos(pos0), pos2 = next_pos(pos1);   // tiles u, u+1, u+2
-  if (NU > 0) {
-    load_ld(pos0);
-    fetch_into(pos0, smem);
-    if (1 < NU) load_ld(pos1);
-  }
 
   u32x4 kreg[NKS], vreg[NKS];
 #pragma unroll
@@ -218,6 +214,10 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
     kreg[ks] = buf_load16(rk, (uint32_t)key * kv_row_bytes + (16 * ks + 8 * hf) * 2);
     vreg[ks] = buf_load16(rv, (uint32_t)key * kv_row_bytes + (16 * ks + 8 * hf) * 2);
   }
+  // the first two tiles; the loop issues each next one two tiles ahead
+  Pos pos0 = first_pos(), pos1 = next_pos(pos0), pos2 = next_pos(pos1);   // tiles u, u+1, u+2
+  if (NU > 0) fetch_into(pos0, smem);
+  if (NU > 1) fetch_into(pos1, smem + STAGE);
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {   // waited for here, not inside the tile loop
     settle(kreg[ks]);
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
   int srow[SWZ ? D / 16 : 1], str_[2][SWZ ? D / 32 : 1];
   if constexpr (SWZ != 0) swz_offsets<D>(lane, srow, str_);
 
-  wait_dma();
+  wait_dma_keep_rt<MAX_PER_TILE>(NU > 1 ? dma_per_tile : 0);   // tile 0 landed; tile 1 may still fly
   __syncthreads();
 
   auto tile = [&](const char* st, int q0, auto edge_tag) {
@@ -249,8 +249,7 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
     const char* qtr = st + tr_q;
     const char* dr = st + OFF_DO + row_q;
     const char* dtr = st + OFF_DO + tr_q;
-    const float* ls = (const float*)(st + OFF_L);
-    const float* dls = (const float*)(st + OFF_D);
+    const char* ldp = st + OFF_LD + 32 * hf;   // this lane half's 4-row groups within a slot
     f32x16 s[NQB], dp[NQB];
     u32x4 ppk[2 * NQB], dspk[2 * NQB];
     // L and D of query group (qb, m) = queries 8m + 4hf .. +3 of block qb, read from LDS
@@ -263,8 +262,12 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
     constexpr int ES = Sched::ES, EU = Sched::EU, LRS = Sched::LRS;
     f32x4 lring[LRS], dring[LRS];
     auto load_grp = [&](int qb, int m) {
-      lring[(4 * qb + m) % LRS] = *(const f32x4*)(ls + qb * 32 + 8 * m + 4 * hf);
-      dring[(4 * qb + m) % LRS] = *(const f32x4*)(dls + qb * 32 + 8 * m + 4 * hf);
+      // rows r0 .. r0+3, r0 = 32 qb + 8 m + 4 hf: slot r0/16, (L, D) pairs from (r0 % 16) * 8
+      const int c0 = qb * 32 + 8 * m;
+      const char* a = ldp + (c0 >> 4) * 256 + (c0 & 15) * 8;
+      const f32x4 x = *(const f32x4*)a, y = *(const f32x4*)(a + 16);
+      lring[(4 * qb + m) % LRS] = f32x4{x[0], x[2], y[0], y[2]};
+      dring[(4 * qb + m) % LRS] = f32x4{x[1], x[3], y[1], y[3]};
     };
     // softmax(qb) element r: P and dS of query 8*(r/4) + 4*hf + r%4 of block qb
     auto sm_elem = [&](int qb, int r) {
@@ -372,16 +375,13 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
   // waves whose keys all follow the tile skip it; the rest need neither. Two loops keep each
   // loop body straight-line (one tile form, no skip branch), so the accumulators stay put.
   // Waves past the end of the sequence compute on zero-filled K, V and store nothing.
-  // One Q tile: DMA of the next tile into stage `nxt` and the math on stage `cur`. The two
-  // stages are distinct, and saying so (restrict) lets the compiler see that the tile's LDS
-  // reads cannot alias the DMA in flight: otherwise it waits for that DMA before the first
-  // transpose read of the tile.
+  // One Q tile: DMA of tile u + 2 into stage `nxt` (the stage tile u - 1 used) and the math
+  // on stage `cur`. The stages are distinct, and saying so (restrict) lets the compiler see
+  // that the tile's LDS reads cannot alias the DMA in flight: otherwise it waits for that
+  // DMA before the first transpose read of the tile.
   auto body = [&](int u, char* __restrict__ nxt, const char* __restrict__ cur, auto edge_tag) {
     constexpr bool EDGE = decltype(edge_tag)::value;
-    if (u + 1 < NU) {
-      fetch_into(pos1, nxt);
-      if (u + 2 < NU) load_ld(pos2);
-    }
+    if (u + 2 < NU) fetch_into(pos2, nxt);
     const int q0 = pos0.qt * BQ;
     if constexpr (EDGE) {
       if (wave_live && q0 + BQ - 1 >= k0w) tile(cur, q0, std::true_type{});
@@ -389,15 +389,19 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
       tile(cur, q0, std::false_type{});
     }
   };
+  int sc = 0;   // stage of tile u (u mod 3)
   auto step = [&](int u, auto edge_tag) {
     pin_all();
-    const int cur = __builtin_amdgcn_readfirstlane((u & 1) * STAGE);
-    body(u, smem + (STAGE - cur), smem + cur, edge_tag);
+    const int cur = __builtin_amdgcn_readfirstlane(sc * STAGE);
+    const int nxt = __builtin_amdgcn_readfirstlane((sc == 0 ? NSTAGE - 1 : sc - 1) * STAGE);
+    body(u, smem + nxt, smem + cur, edge_tag);
     pos0 = pos1;
     pos1 = pos2;
     pos2 = next_pos(pos2);
-    wait_dma();
-    __syncthreads();
+    // tile u + 1 has landed (in every wave, after the barrier); tile u + 2 may still fly
+    wait_dma_keep_rt<MAX_PER_TILE>(u + 2 < NU ? dma_per_tile : 0);
+    ring_barrier();
+    sc = sc == NSTAGE - 1 ? 0 : sc + 1;
     pin_all();
   };
   int u = 0;
@@ -503,8 +507,8 @@ __global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(BwdParams p)
   }
   const bool row_ok = qrow < N;
   const size_t stat_i = stat_row(p.cu, p.T, b, H, h, sv) + qrow;
-  const float lse2 = row_ok ? p.lse[stat_i] * kLog2e : 0.f;
-  const float drow = row_ok ? p.delta[stat_i] : 0.f;
+  const float2 lrow = row_ok ? ((const float2*)p.stats)[stat_i] : float2{0.f, 0.f};
+  const float lse2 = lrow.x, drow = lrow.y;
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {   // waited for here, not inside the tile loop
     settle(qreg[ks]);

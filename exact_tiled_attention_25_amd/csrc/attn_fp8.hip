@@ -316,8 +316,11 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
   // the other multiplies; V(j) is then read one interval later, which one more V stage covers.
   constexpr bool PP = kWaves == 8;
   constexpr int VS = NS + (PP ? 1 : 0);
-  __shared__ __attribute__((aligned(1024))) char smem[NS * TB + VS * TBV];
-  __shared__ float red[kWaves];
+  // One LDS array: the ring stages, then a slot for the per-wave maxima of the V descales.
+  // (With a second __shared__ variable the compiler gives every access to this one the same
+  // alias scope, loses the restrict scopes below, and waits for all DMA before LDS reads.)
+  __shared__ __attribute__((aligned(1024))) char smem[NS * TB + VS * TBV + 4 * kWaves];
+  float* const red = (float*)(smem + NS * TB + VS * TBV);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -342,8 +345,12 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
   const float* dq_h = p.dq + ((size_t)b * H + h) * nblk;
   const float* dk_h = p.dk + ((size_t)b * H + h) * nblk;
   const float* dv_h = p.dv + ((size_t)b * H + h) * nblk;
-  const auto rdk = make_rsrc(dk_h, (uint32_t)nblk * 4);
-  const auto rdv = make_rsrc(dv_h, (uint32_t)nblk * 4);
+  // Per-tile K and V descales by scalar loads: a uniform address in the constant address
+  // space (the kernel never writes them). A vector load would count on vmcnt with the tile
+  // DMA, and the wait for its value would also wait for every DMA issued before the use.
+  using cfloat = const __attribute__((address_space(4))) float;
+  cfloat* dk_s = (cfloat*)dk_h;
+  cfloat* dv_s = (cfloat*)dv_h;
 
   // largest V descale of the head (before any DMA is in flight)
   float dvm = 0.f;
@@ -399,10 +406,10 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
     for (int t = 1; t <= NS - 2; ++t) keep += (j + t < nkt ? n_wv : 0) + (j + t + 1 < nkt ? n_w : 0);
     wait_dma_keep_rt<KEEP_MAX>(keep);
   };
-  // per-tile descale factors, loaded one tile ahead (before that iteration's DMA batch)
+  // per-tile descale factors, loaded one tile ahead (t < nkt <= nblk)
   auto load_desc = [&](int t, float& dk, float& dv) {
-    dk = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdk, (uint32_t)t * 4, 0, 0));
-    dv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdv, (uint32_t)t * 4, 0, 0));
+    dk = dk_s[t];
+    dv = dv_s[t];
   };
   float dk_c, dv_c;   // descales of the tile the next iteration exponentiates
   load_desc(0, dk_c, dv_c);
@@ -483,7 +490,7 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
     mx_next = tile_max(sc, coef_c);
   }
   // the first prefetch overwrites the stage of K(0), which the prologue just read
-  __syncthreads();
+  ring_barrier();
 
   auto prefetch = [&](int j) {
     if (j + NS - 1 < nkt) dma_v(j + NS - 1);
@@ -491,7 +498,7 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
   };
   auto end_tile = [&](int j) {
     wait_before(j + 1);
-    __syncthreads();
+    ring_barrier();
   };
   auto rescale = [&]() {
     const float m_cand = fmaxf(m_run, mx_next);
@@ -519,13 +526,16 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
   constexpr int PF = 2;
   static_assert(EPS * S1 == 16 * NKB && MPS * S2 == 16 * NKB && EPS % 4 == 0 && MPS % 2 == 0, "step split");
   float dk_n, dv_n;
-  auto fast_iter = [&](auto late, int jj, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB]) __attribute__((always_inline)) {
+  // kn, vc: K(jj+1) and V(jj) in LDS, this lane's bases; restrict, so that the compiler can
+  // tell their reads from the stages the DMA in flight is filling (otherwise it waits for
+  // every outstanding DMA before the first read, which drains the ring's prefetch each tile).
+  auto fast_iter = [&](auto late, int jj, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB], const char* __restrict__ kn,
+                       const char* __restrict__ vc, char* __restrict__ kd, char* __restrict__ vd) __attribute__((always_inline)) {
     load_desc(jj + 1 < nkt ? jj + 1 : jj, dk_n, dv_n);
-    prefetch(jj);
+    if (jj + NS - 1 < nkt) dma_issue<VPlan, kWaves>(vvoff, vd, vbase, (jj + NS - 1) * BC, row_bytes, nrec, wave);
+    if (jj + NS < nkt) dma_issue<Plan, kWaves>(voff, kd, kbase, (jj + NS) * BC, row_bytes, nrec, wave);
     rescale();
     const float bias = logw_c - m_run;
-    const char* kn = kst(jj + 1) + k_lane;
-    const char* vc = vst(jj) + v_lane;
     i32x8 pk;
     i32x8 kop[S1];
     float e[16 * NKB];
@@ -553,7 +563,7 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
     if constexpr (decltype(late)::value) end_tile(jj);
     const float coef_n = cq * dk_n;
     i32x8 vop[S2];
-    float mx = -INFINITY, psum = 0.f;
+    float mx = -INFINITY;
     const float rsum = rowsum_f8(sel, pk);
 #pragma unroll
     for (int t = 0; t < PF && t < S2; ++t) vop[t] = lds_vt8<PV8>(vc, t);
@@ -581,11 +591,11 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
   int j = 0;
   auto fast_loop = [&](auto late) __attribute__((always_inline)) {
     for (; j + 2 < nkt_w && !is_edge(j + 2); j += 2) {
-      fast_iter(late, j, sc, sn);
-      fast_iter(late, j + 1, sn, sc);
+      fast_iter(late, j, sc, sn, kst(j + 1) + k_lane, vst(j) + v_lane, kst(j + NS), vst(j + NS - 1));
+      fast_iter(late, j + 1, sn, sc, kst(j + 2) + k_lane, vst(j + 1) + v_lane, kst(j + 1 + NS), vst(j + NS));
     }
     if (j + 1 < nkt_w && !is_edge(j + 1)) {
-      fast_iter(late, j, sc, sn);
+      fast_iter(late, j, sc, sn, kst(j + 1) + k_lane, vst(j) + v_lane, kst(j + NS), vst(j + NS - 1));
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) sc[kb] = sn[kb];
       ++j;
@@ -622,9 +632,11 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
         }
       l_run = fmaf(psum, rw_c, l_run);
       l_rnd = fmaf(rowsum_f8(sel, pk), rw_c, l_rnd);
-      const char* vc = vst(j) + v_lane;
+      // V(j) through a restrict pointer, as in the fast iteration
+      [&](const char* __restrict__ vc) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < NDB; ++i) oacc[i] = mfma_f8_scaled(lds_vt8<PV8>(vc, i), pk, oacc[i], sc_c);
+        for (int i = 0; i < NDB; ++i) oacc[i] = mfma_f8_scaled(lds_vt8<PV8>(vc, i), pk, oacc[i], sc_c);
+      }(vst(j) + v_lane);
       if (j + 1 < nkt_w) {
         tile_scores(sc, kst(j + 1) + k_lane);
         if (is_edge(j + 1)) tile_mask(sc, (j + 1) * BC);

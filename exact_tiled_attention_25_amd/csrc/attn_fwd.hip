@@ -123,9 +123,12 @@ __device__ __forceinline__ float tile_exp(const f32x16 (&s)[NKB], u32x4 (&pk)[2 
   return psum;
 }
 
-// O^T += V^T P^T for one tile (V row-major in LDS, gathered by transpose reads).
+// O^T += V^T P^T for one tile (V row-major in LDS, gathered by transpose reads). `vl` is
+// restrict: the compiler can then tell that these reads do not touch the stages the DMA in
+// flight is filling; otherwise it waits for every outstanding DMA (vmcnt(0)) before the
+// first transpose read, which drains the ring's prefetch every tile.
 template <bool BF16, int D, int NKB>
-__device__ __forceinline__ void tile_pv(f32x16 (&oacc)[D / 32], const char* vl, const u32x4 (&pk)[2 * NKB]) {
+__device__ __forceinline__ void tile_pv(f32x16 (&oacc)[D / 32], const char* __restrict__ vl, const u32x4 (&pk)[2 * NKB]) {
 #pragma unroll
   for (int i = 0; i < D / 32; ++i)
 #pragma unroll
@@ -271,7 +274,7 @@ __global__ __launch_bounds__((fwd_threads<D, SMALL>()), (fwd_wgs<D, SMALL>())) v
     mx_next = tile_max<NKB>(sc, c);
   }
   // the first prefetch overwrites the stage of K(0), which the prologue just read
-  __syncthreads();
+  ring_barrier();
 
   auto prefetch = [&](int j) {
     if (j + NS - 1 < nkt) dma_v(j + NS - 1);
@@ -280,7 +283,7 @@ __global__ __launch_bounds__((fwd_threads<D, SMALL>()), (fwd_wgs<D, SMALL>())) v
   // End of iteration j: iteration j+1 reads K(j+2) and V(j+1).
   auto end_tile = [&](int j) {
     wait_before(j + 1);
-    __syncthreads();
+    ring_barrier();
   };
   // the maximum of tile j (taken one step earlier) may move the reference: rescale O and l
   auto rescale = [&]() {
@@ -346,9 +349,9 @@ __global__ __launch_bounds__((fwd_threads<D, SMALL>()), (fwd_wgs<D, SMALL>())) v
     }
   };
   // Block 2 of tile jj: O^T += V(jj)^T P~(jj)^T, the row sum of P~(jj), and the row maximum
-  // of the scores nxt = S(jj+1) that block 1 of tile jj produced.
-  auto blk2 = [&](int jj, const f32x16 (&nxt)[NKB]) __attribute__((always_inline)) {
-    const char* vc = vst(jj) + v_lane;
+  // of the scores nxt = S(jj+1) that block 1 of tile jj produced. `vc` (V(jj) in LDS, this
+  // lane's base) is restrict for the reason given at tile_pv.
+  auto blk2 = [&](const char* __restrict__ vc, const f32x16 (&nxt)[NKB]) __attribute__((always_inline)) {
     u32x4 vop[S2];
     float mx = -INFINITY, psum = 0.f;
     __builtin_amdgcn_sched_barrier(0);
@@ -400,7 +403,7 @@ __global__ __launch_bounds__((fwd_threads<D, SMALL>()), (fwd_wgs<D, SMALL>())) v
     rescale();
     blk1(jj, cur, nxt);
     if constexpr (decltype(late)::value) end_tile(jj);
-    blk2(jj, nxt);
+    blk2(vst(jj) + v_lane, nxt);
     if constexpr (!decltype(late)::value) end_tile(jj);
   };
   int j = 0;

@@ -38,12 +38,13 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;  // workspace: rowsum(dO o O), [B][H][N]
+  // workspace: per row the pair (L log2 e, D = rowsum(dO o O)), fp32 [B][H][N][2]
+  float* stats;
   int B, H, N;
   float scale;
   float c;  // scale * log2(e)
   int Hkv;  // key/value heads (divides H); dK, dV are [B][N][Hkv][d]
-  const int* cu;  // variable-length batches as in FwdParams (then D is [H][T] too)
+  const int* cu;  // variable-length batches as in FwdParams (then stats is [H][T][2])
   int T;
 };
 

@@ -95,6 +95,12 @@ __device__ __forceinline__ void dma_issue(const uint32_t* voff, char* dst, const
   }
 }
 
+// Number of DMA instructions dma_issue makes in wave `wave` for one tile.
+template <class Plan, int NWAVES>
+__device__ __forceinline__ int dma_count(int wave) {
+  return Plan::NI % NWAVES == 0 ? Plan::NPW : (Plan::NI - wave + NWAVES - 1) / NWAVES;
+}
+
 // Generic forms for a tile of row pitch PITCH bytes.
 // Row reads (MFMA operand over dims): lane base l%32 rows, 16-byte chunk l/32; then
 // rows blk*32 + l%32, dims 16*ks + 8*(l/32) .. +7 are at base + blk*32*PITCH + ks*32.
@@ -167,6 +173,19 @@ template <int N>
 __device__ __forceinline__ void wait_dma_keep() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier between the tiles of a DMA ring. __syncthreads() is s_barrier between a
+// release and an acquire fence, and the compiler completes the release by waiting for every
+// LDS DMA in flight (vmcnt(0)), the tiles prefetched further ahead included. This barrier
+// takes only what a ring needs: each wave has already waited for its own part of the tile
+// the next step reads (wait_dma_keep*); its LDS reads are complete (lgkmcnt(0)) before any
+// wave passes, so that no later DMA into a stage overtakes a read of it; and the empty asm
+// with a memory clobber keeps the compiler from moving LDS accesses across.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // The same for a wave-uniform count 0 <= n <= MAX (s_waitcnt takes an immediate; counts

@@ -79,7 +79,8 @@ attn_status_t attn_fwd_varlen(const void* q, const void* k, const void* v, void*
                               int d, int causal, float scale, attn_dtype_t dtype,
                               attn_stream_t stream);
 
-/* Bytes of device workspace attn_bwd_varlen needs: fp32 D, [H][T]. */
+/* Bytes of device workspace attn_bwd_varlen needs: the per-row fp32 pairs (L log2 e,
+ * D = rowsum(dO o O)), [H][T][2]. */
 size_t attn_bwd_varlen_workspace_bytes(int T, int H);
 
 /* Backward of attn_fwd_varlen: layouts as there; dq [T][H][d], dk, dv [T][H_kv][d]. */
@@ -109,7 +110,8 @@ attn_status_t attn_fwd_splitkv(const void* q, const void* k, const void* v, void
                                attn_dtype_t dtype, int num_splits, void* workspace,
                                size_t workspace_bytes, attn_stream_t stream);
 
-/* Bytes of device workspace attn_bwd needs: fp32 D = rowsum(dO o O), [B][H][N]. */
+/* Bytes of device workspace attn_bwd needs: the per-row fp32 pairs (L log2 e,
+ * D = rowsum(dO o O)), [B][H][N][2]. */
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
 
 /* Backward pass with LSE recomputation (Deep Dive "Backward warp specialization": S and P
@@ -126,9 +128,9 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): attn_bwd with no workspace argument.
  * Same arguments, kernels, results (bit for bit) and errors as attn_bwd; the per-row
- * statistic D lives in a fixed library-owned device array of attn_bwd_noalloc_max_rows()
- * fp32 entries (4 Mi rows, 16 MiB, held by each GPU the library runs on until the process
- * ends). B*H*N above that limit returns ATTN_ETOOLARGE. Nothing is allocated, also not on
+ * statistics (two fp32 a row) live in a fixed library-owned device array of
+ * attn_bwd_noalloc_max_rows() rows (4 Mi rows, 32 MiB, held by each GPU the library runs on
+ * until the process ends). B*H*N above that limit returns ATTN_ETOOLARGE. Nothing is allocated, also not on
  * the first call on a device (which looks up the array's device address). Every call on
  * one GPU shares that array: calls that may overlap on the same GPU (different streams,
  * host threads) race and must be ordered by the caller. ATTN_ELAUNCH if the array's device

@@ -35,7 +35,7 @@ def test_strerror_covers_every_status(lib):
 
 
 def test_workspace_size(lib):
-    assert lib.attn_bwd_workspace_bytes(2, 16, 8192, 128) == 2 * 16 * 8192 * 4
+    assert lib.attn_bwd_workspace_bytes(2, 16, 8192, 128) == 2 * 16 * 8192 * 8
     assert lib.attn_bwd_workspace_bytes(0, 16, 8192, 128) == 0
 
 
@@ -81,7 +81,7 @@ def test_null_pointers_rejected(lib):
     assert lib.attn_fwd_varlen(None, None, None, None, None, None, 2, 0, 64, 4, 2, 64, 0, 0.125, 0, None) == 0
     assert lib.attn_bwd_varlen(None, None, None, None, None, None, None, None, None, None, 2, 100, 64, 4, 3, 64, 0,
                                0.125, 0, None, 0, None) == 1
-    assert lib.attn_bwd_varlen_workspace_bytes(100, 4) == 1600
+    assert lib.attn_bwd_varlen_workspace_bytes(100, 4) == 3200
     assert lib.attn_fwd_splitkv(None, None, None, None, None, 1, 1, 16, 64, 0, 0.125, 0, 2, None, 0, None) == 1
     assert lib.attn_fwd_splitkv(None, None, None, None, None, 1, 1, 16, 64, 0, 0.125, 0, 0, None, 0, None) == 1
     assert lib.attn_fwd_splitkv(None, None, None, None, None, 1, 1, 16, 96, 0, 0.125, 0, 2, None, 0, None) == 2
