@@ -224,6 +224,21 @@ def peak_probe(torch, dev):
             res[f"{name}_cycles" + ("" if wps == 2 else "_one_wave")] = round(cyc / (wps * iters * 16), 2)
             clocks.append(cyc / real * 0.1)   # s_memrealtime runs at 100 MHz
     res["probe_clock_ghz"] = round(float(np.median(clocks)), 3)
+    # fp32 atomic adds vs plain stores of 64 x 128 dQ tiles, per (head, 128-key tile): what
+    # accumulating dQ from the key-outer pass would cost at B=2 N=8192 H=16 d=128, where
+    # every one of the 64 key tiles of a head adds N x d fp32 (8.6 GB in all)
+    L.probe_atomic.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                               ctypes.POINTER(ctypes.c_float)]
+    ws = torch.zeros(2 * 8192 * 16 * 128, dtype=torch.float32, device=dev)
+    nqt = 32
+    for mode, name in ((0, "atomic_add_f32"), (1, "store_f32")):
+        rc = L.probe_atomic(mode, ws.data_ptr(), 4, stream, ctypes.byref(ms))   # warm
+        rc |= L.probe_atomic(mode, ws.data_ptr(), nqt, stream, ctypes.byref(ms))
+        if rc:
+            raise RuntimeError(f"probe_atomic failed ({rc})")
+        res[f"{name}_tbps"] = round(2048 * nqt * 64 * 128 * 4 / (ms.value * 1e-3) / 1e12, 3)
+    dq_bytes = 64 * 2 * 16 * 8192 * 128 * 4
+    res["dq_atomic_accumulate_ms_bench_shape"] = round(dq_bytes / (res["atomic_add_f32_tbps"] * 1e12) * 1e3, 3)
     return res
 
 

@@ -434,11 +434,12 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
 // VALU underneath; dQ^T += K^T dS^T (K read transposed) with dS = P o (dP - D) of the next
 // 16-key chunk computed underneath. Tiles that touch the diagonal or the ragged end zero
 // the masked P explicitly.
-template <int D> struct DqCfg { static constexpr int BC = 64, OCC = 2; };
-template <> struct DqCfg<256> { static constexpr int BC = 64, OCC = 1; };   // 64 keys: 15% faster than 32 at d = 256
+template <int D> struct DqCfg { static constexpr int BC = 64, OCC = 2, WAVES = 4; };
+template <> struct DqCfg<256> { static constexpr int BC = 64, OCC = 1, WAVES = 4; };   // 64 keys: 15% faster than 32 at d = 256
 
 template <bool BF16, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, DqCfg<D>::OCC) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(64 * DqCfg<D>::WAVES, DqCfg<D>::OCC) void bwd_dq_kernel(BwdParams p) {
+  constexpr int kWaves = DqCfg<D>::WAVES;
   constexpr int BC = DqCfg<D>::BC;
   constexpr int NKB = BC / 32;
   constexpr int NKS = D / 16;
@@ -644,8 +645,9 @@ hipError_t launch_t(const BwdParams& p, hipStream_t s) {
   const int nkvt = (p.N + kWaves * 32 - 1) / (kWaves * 32);
   hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, CAUSAL>), dim3((unsigned)(p.B * p.Hkv * nkvt)), dim3(256), 0, s, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int nqt = (p.N + kWaves * 32 - 1) / (kWaves * 32);
-  hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, CAUSAL>), dim3((unsigned)(p.B * p.H * nqt)), dim3(256), 0, s, p);
+  constexpr int qw = DqCfg<D>::WAVES;
+  const int nqt = (p.N + qw * 32 - 1) / (qw * 32);
+  hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, CAUSAL>), dim3((unsigned)(p.B * p.H * nqt)), dim3(64 * qw), 0, s, p);
   return hipGetLastError();
 }
 

@@ -374,9 +374,6 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
     qreg[ks] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
   }
   const float cq = p.c * (qrow < N ? dq_h[qrow >> 6] : 1.0f);
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) settle(qreg[ks]);   // waited for here, not inside the tile loop
-  settle(cq);
 
   const int kend = CAUSAL ? min(N, (qt + 1) * kBR) : N;
   const int nkt = (kend + BC - 1) / BC;
@@ -438,6 +435,11 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
     if (t < nkt) dma_v(t);
     if (t + 1 < nkt) dma_k(t + 1);
   }
+  // Q (and its descale) waited for here, not inside the tile loop, and only now: the load
+  // and the first tiles' DMA share one HBM round trip
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) settle(qreg[ks]);
+  settle(cq);
 
   set_weight(dv_c);
   f32x16 oacc[NDB];

@@ -9,6 +9,11 @@
 //    independent registers per wave, so latency is hidden), from s_memtime, and the shader
 //    clock during the loop from the ratio of s_memtime to the fixed-rate s_memrealtime
 //    (100 MHz).
+//  * probe_atomic: fp32 global atomic adds (or plain stores) of 64 x 128 tiles into a
+//    [2][8192][16][128] fp32 accumulator, one workgroup per (head, 128-key tile) walking
+//    nqt query tiles: the traffic a key-outer backward would make to accumulate dQ
+//    across its key tiles, to price that design against recomputing S and dP in a
+//    separate query-outer pass.
 // Built into libattn_probe.so, loaded only by bench.py.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -160,9 +165,50 @@ __global__ __launch_bounds__(64) void mfma_once_kernel(int kind, const uint32_t*
   for (int r = 0; r < 16; ++r) d[l * 16 + r] = acc[r];
 }
 
+// MODE 0: global_atomic_add_f32 (no return), 1: plain store. Workgroup w: head w / 64
+// (b = head / 16, h = head % 16), 128-key tile w % 64; wave rows 16 per query tile.
+template <int MODE>
+__global__ __launch_bounds__(256) void atomic_probe_kernel(float* ws, int nqt) {
+  const int head = blockIdx.x / 64;
+  const int b = head / 16, h = head % 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int qt = 0; qt < nqt; ++qt) {
+#pragma unroll 4
+    for (int i = 0; i < 32; ++i) {
+      const int row = qt * 64 + wave * 16 + (i >> 1);   // < 64 nqt <= 8192
+      const int d = (i & 1) * 64 + lane;                // < 128
+      float* p = ws + (((size_t)b * 8192 + row) * 16 + h) * 128 + d;
+      if (MODE == 0) __hip_atomic_fetch_add(p, 1.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else *p = 1.0f;
+    }
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+// 2048 workgroups (32 heads x 64 key tiles), each adding (mode 0) or storing (mode 1) nqt
+// 64 x 128 fp32 tiles (1 <= nqt <= 128) into ws, which holds 2 * 8192 * 16 * 128 floats of
+// device memory; *ms = elapsed time on `stream` (HIP events). Returns a hipError_t.
+int probe_atomic(int mode, float* ws, int nqt, void* stream, float* ms) {
+  if (nqt < 1 || nqt > 128 || (mode != 0 && mode != 1)) return (int)hipErrorInvalidValue;
+  hipStream_t s = (hipStream_t)stream;
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return (int)hipErrorUnknown;
+  hipError_t err = hipEventRecord(e0, s);
+  if (err == hipSuccess) {
+    if (mode == 0) hipLaunchKernelGGL(atomic_probe_kernel<0>, dim3(2048), dim3(256), 0, s, ws, nqt);
+    else hipLaunchKernelGGL(atomic_probe_kernel<1>, dim3(2048), dim3(256), 0, s, ws, nqt);
+    err = hipGetLastError();
+  }
+  if (err == hipSuccess) err = hipEventRecord(e1, s);
+  if (err == hipSuccess) err = hipEventSynchronize(e1);
+  if (err == hipSuccess) err = hipEventElapsedTime(ms, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  return (int)err;
+}
 
 // One wave, one MFMA (see mfma_once_kernel); synchronises the stream.
 int probe_mfma_once(int kind, const void* a, const void* b, const float* c, float* d, int sb, void* stream) {
