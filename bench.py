@@ -239,6 +239,16 @@ def peak_probe(torch, dev):
         res[f"{name}_tbps"] = round(2048 * nqt * 64 * 128 * 4 / (ms.value * 1e-3) / 1e12, 3)
     dq_bytes = 64 * 2 * 16 * 8192 * 128 * 4
     res["dq_atomic_accumulate_ms_bench_shape"] = round(dq_bytes / (res["atomic_add_f32_tbps"] * 1e12) * 1e3, 3)
+    # LDS read bytes per clock per CU (8 waves, conflict-free): 16-byte row chunks and the
+    # transposed 8-byte reads the P~V and backward products use
+    L.probe_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lds_out = torch.empty(256 * 8, dtype=torch.int64, device=dev)
+    iters = 2048
+    for kind, name, bytes_per in ((0, "lds_read_b128_bytes_per_clk_cu", 1024), (1, "lds_read_tr16_bytes_per_clk_cu", 512)):
+        if L.probe_lds(kind, 64, stream, lds_out.data_ptr()) or L.probe_lds(kind, iters, stream, lds_out.data_ptr()):
+            raise RuntimeError("probe_lds failed")
+        cyc = float(np.median(lds_out.cpu().numpy().astype(np.float64)))
+        res[name] = round(bytes_per * iters * 8 * 8 / cyc, 1)
     return res
 
 

@@ -14,6 +14,10 @@
 //    nqt query tiles: the traffic a key-outer backward would make to accumulate dQ
 //    across its key tiles, to price that design against recomputing S and dP in a
 //    separate query-outer pass.
+//  * probe_lds: LDS read throughput with eight waves per CU, for the two operand reads the
+//    attention kernels issue: ds_read_b128 of 16-byte row chunks at the K-tile pitch
+//    (2d + 16 bytes at d = 128) and ds_read_b64_tr_b16 at the V-tile pitch (2d + 64), both
+//    conflict-free by construction, eight reads in flight per wave, timed with s_memtime.
 // Built into libattn_probe.so, loaded only by bench.py.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -184,9 +188,58 @@ __global__ __launch_bounds__(256) void atomic_probe_kernel(float* ws, int nqt) {
   }
 }
 
+// KIND 0: ds_read_b128, 1: ds_read_b64_tr_b16. 80 KiB of LDS (one workgroup per CU), 8
+// waves; out[block * 8 + wave] = s_memtime cycles of the wave's loop.
+template <int KIND>
+__global__ __launch_bounds__(512, 1) void lds_probe_kernel(unsigned long long* out, int iters) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(1024))) char buf[81920];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < 81920 / 4; i += 512) ((uint32_t*)buf)[i] = mix((uint32_t)i);
+  __syncthreads();
+  const int i16 = lane & 15, grp = lane >> 4, hf = grp >> 1;
+  // row chunks: rows l%32 at pitch 272, chunk l/32; transposed: rows 4hf + i16/4 at pitch
+  // 320, dims 16 (grp%2) + 4 (i16%4). Largest byte read: 3*20480 + 8448 + 224 + 8704 + 16
+  // (rows) and 3*20480 + 2296 + 448 + 5120 + 8 (transposed), both inside the 80 KiB.
+  const int off = KIND == 0 ? (lane & 31) * 272 + (lane >> 5) * 16
+                            : (4 * hf + (i16 >> 2)) * 320 + (16 * (grp & 1) + 4 * (i16 & 3)) * 2;
+  const char* base = buf + (wave & 3) * 20480 + off;
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+    if (KIND == 0) {
+      u32x4 v[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) v[r] = *(const u32x4*)(base + r * 32 + (it & 1) * 8704);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) asm volatile("" ::"v"(v[r]));
+    } else {
+      s16x4 v[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        v[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base + r * 64 + (it & 1) * 5120));
+#pragma unroll
+      for (int r = 0; r < 8; ++r) asm volatile("" ::"v"(v[r]));
+    }
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  if (lane == 0) out[blockIdx.x * 8 + wave] = t1 - t0;
+}
+
 }  // namespace
 
 extern "C" {
+
+// 256 workgroups (one per CU) of 8 waves, each wave iters x 8 reads; out: 2048 uint64 of
+// device memory (per-wave cycles). Synchronises the stream. Returns a hipError_t.
+int probe_lds(int kind, int iters, void* stream, unsigned long long* out) {
+  hipStream_t s = (hipStream_t)stream;
+  if (kind == 0) hipLaunchKernelGGL(lds_probe_kernel<0>, dim3(256), dim3(512), 0, s, out, iters);
+  else hipLaunchKernelGGL(lds_probe_kernel<1>, dim3(256), dim3(512), 0, s, out, iters);
+  hipError_t err = hipGetLastError();
+  if (err == hipSuccess) err = hipStreamSynchronize(s);
+  return (int)err;
+}
 
 // 2048 workgroups (32 heads x 64 key tiles), each adding (mode 0) or storing (mode 1) nqt
 // 64 x 128 fp32 tiles (1 <= nqt <= 128) into ws, which holds 2 * 8192 * 16 * 128 floats of

@@ -117,3 +117,14 @@ def test_non_finite_scale_rejected_with_pointers(lib):
         assert lib.attn_fwd_fp8(*fake[:5], 1, 1, 16, 64, 0, bad, *fake[:3], 0, 0, None) == 1
     for base in (float("nan"), float("inf")):
         assert lib.attn_fp8_quantize_rope(*fake[:3], 1, 1, 16, 64, 0, base, 1, 0, None) == 1
+
+
+def test_probe_library_exports_its_probes():
+    """The measurement probes bench.py reports (matrix-core ceiling, VALU costs, LDS read
+    rates, fp32 atomic rate) are built into their own library and load without a device."""
+    path = os.path.join(ROOT, "exact_tiled_attention_25_amd", "libattn_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("libattn_probe.so is not built")
+    probe = ctypes.CDLL(path)
+    for name in ("probe_mfma", "probe_mfma_once", "probe_valu", "probe_lds", "probe_atomic"):
+        assert hasattr(probe, name), name
