@@ -401,7 +401,13 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
     int keep = 0;
 #pragma unroll
     for (int t = 1; t <= NS - 2; ++t) keep += (j + t < nkt ? n_wv : 0) + (j + t + 1 < nkt ? n_w : 0);
-    wait_dma_keep_rt<KEEP_MAX>(keep);
+    // Away from the end of the key range every tile of the batch exists: keep the count
+    // of the waves with the fewest DMA instructions, a constant. The other waves then also
+    // wait for the first one or two of their batch, issued at the start of the tile
+    // (waiting longer is always safe); a count chosen at run time would cost a chain of
+    // compares and branches per tile.
+    if (j + NS - 1 < nkt) wait_dma_keep<(NS - 2) * (KMIN + KMINV)>();
+    else wait_dma_keep_rt<KEEP_MAX>(keep);
   };
   // per-tile descale factors, loaded one tile ahead (t < nkt <= nblk)
   auto load_desc = [&](int t, float& dk, float& dv) {
@@ -528,6 +534,10 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
   constexpr int PF = 2;
   static_assert(EPS * S1 == 16 * NKB && MPS * S2 == 16 * NKB && EPS % 4 == 0 && MPS % 2 == 0, "step split");
   float dk_n, dv_n;
+  // P~ operand of the fast tiles. Kept across tiles: each conversion writes half of a word
+  // whose other half it keeps, and the word it lands in is last tile's (already consumed),
+  // so no register has to be cleared first.
+  i32x8 pk = {};
   // kn, vc: K(jj+1) and V(jj) in LDS, this lane's bases; restrict, so that the compiler can
   // tell their reads from the stages the DMA in flight is filling (otherwise it waits for
   // every outstanding DMA before the first read, which drains the ring's prefetch each tile).
@@ -538,7 +548,6 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
     if (jj + NS < nkt) dma_issue<Plan, kWaves>(voff, kd, kbase, (jj + NS) * BC, row_bytes, nrec, wave);
     rescale();
     const float bias = logw_c - m_run;
-    i32x8 pk;
     i32x8 kop[S1];
     float e[16 * NKB];
     float psum_a = 0.f, psum_b = 0.f;
@@ -554,7 +563,10 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
       for (int u = 0; u < EPS; ++u) {
         const int i = EPS * t + u;
         e[i] = fast_exp2(fmaf(cur[i >> 4][i & 15], coef_c, bias));
-        if ((i & 3) == 3) pk[i >> 2] = (int)cvt4_fp8(e[i - 3], e[i - 2], e[i - 1], e[i]);
+        if ((i & 3) == 3) {
+          const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e[i - 3], e[i - 2], pk[i >> 2], false);
+          pk[i >> 2] = __builtin_amdgcn_cvt_pk_fp8_f32(e[i - 1], e[i], lo, true);
+        }
         if (i & 1) psum_b += e[i]; else psum_a += e[i];
       }
       pin(psum_a);

@@ -243,7 +243,13 @@ __global__ __launch_bounds__((fwd_threads<D, SMALL>()), (fwd_wgs<D, SMALL>())) v
     int keep = 0;
 #pragma unroll
     for (int t = 1; t <= NS - 2; ++t) keep += (j + t < nkt ? nv_w : 0) + (j + t + 1 < nkt ? nk_w : 0);
-    wait_dma_keep_rt<KEEP_MAX>(keep);
+    // Away from the end of the key range every tile of the batch exists: keep the count
+    // of the waves with the fewest DMA instructions, a constant. The other waves then also
+    // wait for the first one or two of their batch, issued at the start of the tile
+    // (waiting longer is always safe); a count chosen at run time would cost a chain of
+    // compares and branches per tile.
+    if (j + NS - 1 < nkt) wait_dma_keep<(NS - 2) * (KMIN + VMIN)>();
+    else wait_dma_keep_rt<KEEP_MAX>(keep);
   };
   if (nkt > 0) dma_k(0);   // a split-KV part can be empty: then no tile is loaded at all
 
