@@ -205,6 +205,27 @@ def test_fp8_matches_kernel_model(lib, shape, causal, out):
                  emul=_emulator(codes, causal, scale) if N >= 500 else None)
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_fp8_d256_reference_moves_inside_fast_tiles(lib, causal):
+    """d = 256 (four waves, one per SIMD; each tile's softmax split over two iterations, the
+    rescale decision taken one tile ahead): keys scaled up along the sequence, so that the
+    row maxima grow from tile to tile and the reference moves at many tiles inside the
+    pipelined iterations, with paired iterations, an odd last one and a ragged tail. The
+    ramp to 2x moves the reference at about half the (group, tile) steps after the first;
+    a steeper one doubles the scores again, and the matrix core's inexact addition of the
+    e4m3 products then moves L by up to 2.2e-4 on every FP8 kernel, over the 2e-4 gate."""
+    B, N, H, d = 1, 1100, 2, 256
+    log(f"fp8 d=256 growing scores causal={causal}")
+    x = workloads.make_inputs(B, N, H, d, "bf16", 46)
+    ramp = torch.linspace(1.0, 2.0, N).view(1, N, 1, 1)
+    x["k"] = (x["k"].float() * ramp).to(torch.bfloat16)
+    codes = _codes_for(x)
+    scale = 1 / np.sqrt(d)
+    o, lse = _fwd(codes, causal, scale)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    _model_check(o, lse, codes, causal, scale, [(0, 0), (0, 1)], np.arange(N), "bf16")
+
+
 @pytest.mark.parametrize("factors", [{2: 100.0}, {1: 0.01, 4: 30.0}], ids=["x100", "x0.01_x30"])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 def test_fp8_v_blocks_of_different_scale(lib, factors, causal):
