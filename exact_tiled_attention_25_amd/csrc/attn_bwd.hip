@@ -410,20 +410,31 @@ __global__ __launch_bounds__(256, DkvCfg<D>::OCC) void bwd_dkdv_kernel(BwdParams
   }
   for (; u < NU; ++u) step(u, std::false_type{});
 
+  // dV, then dK, leave through the ring's LDS, each wave in its own area (the last step
+  // waited for every DMA and passed a barrier after every wave's last operand read).
+  using OStage = RowStage<2 * D>;
+  static_assert(kWaves * OStage::BYTES <= (int)sizeof(smem), "dK/dV staging fits the ring");
   if (wave_live) {
     const float scale = p.scale;
+    char* ost = smem + wave * OStage::BYTES;
 #pragma unroll
     for (int i = 0; i < NDB; ++i)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int d0 = i * 32 + 8 * rr + 4 * hf;
-        const u32x2 vv = {pack2<BF16>(dvacc[i][4 * rr + 0], dvacc[i][4 * rr + 1]),
-                          pack2<BF16>(dvacc[i][4 * rr + 2], dvacc[i][4 * rr + 3])};
-        const u32x2 kk = {pack2<BF16>(dkacc[i][4 * rr + 0] * scale, dkacc[i][4 * rr + 1] * scale),
-                          pack2<BF16>(dkacc[i][4 * rr + 2] * scale, dkacc[i][4 * rr + 3] * scale)};
-        buf_store8(rdv, (uint32_t)key * kv_row_bytes + d0 * 2, vv);
-        buf_store8(rdk, (uint32_t)key * kv_row_bytes + d0 * 2, kk);
+        OStage::put(ost, l32, d0 * 2, u32x2{pack2<BF16>(dvacc[i][4 * rr + 0], dvacc[i][4 * rr + 1]),
+                                            pack2<BF16>(dvacc[i][4 * rr + 2], dvacc[i][4 * rr + 3])});
       }
+    OStage::store(ost, rdv, (uint32_t)k0w, kv_row_bytes, 0, lane);
+#pragma unroll
+    for (int i = 0; i < NDB; ++i)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int d0 = i * 32 + 8 * rr + 4 * hf;
+        OStage::put(ost, l32, d0 * 2, u32x2{pack2<BF16>(dkacc[i][4 * rr + 0] * scale, dkacc[i][4 * rr + 1] * scale),
+                                            pack2<BF16>(dkacc[i][4 * rr + 2] * scale, dkacc[i][4 * rr + 3] * scale)});
+      }
+    OStage::store(ost, rdk, (uint32_t)k0w, kv_row_bytes, 0, lane);
   }
 }
 
@@ -619,19 +630,22 @@ __global__ __launch_bounds__(64 * DqCfg<D>::WAVES, DqCfg<D>::OCC) void bwd_dq_ke
     __syncthreads();
   }
 
+  // dQ leaves through the ring's LDS, each wave in its own area (the loop ended with a DMA
+  // wait and a barrier).
+  using OStage = RowStage<2 * D>;
+  static_assert(kWaves * OStage::BYTES <= (int)sizeof(smem), "dQ staging fits the ring");
   if (nkt_w > 0) {
     const float scale = p.scale;
+    char* ost = smem + wave * OStage::BYTES;
 #pragma unroll
     for (int i = 0; i < NDB; ++i)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int d0 = i * 32 + 8 * rr + 4 * hf;
-        const u32x2 vv = {pack2<BF16>(dqacc[i][4 * rr + 0] * scale, dqacc[i][4 * rr + 1] * scale),
-                          pack2<BF16>(dqacc[i][4 * rr + 2] * scale, dqacc[i][4 * rr + 3] * scale)};
-        buf_store8(rdq, (uint32_t)qrow * row_bytes + d0 * 2, vv);
+        OStage::put(ost, l32, d0 * 2, u32x2{pack2<BF16>(dqacc[i][4 * rr + 0] * scale, dqacc[i][4 * rr + 1] * scale),
+                                            pack2<BF16>(dqacc[i][4 * rr + 2] * scale, dqacc[i][4 * rr + 3] * scale)});
       }
-  } else if (q0 < N) {
-    // a wave whose rows see no key tile (cannot happen for equal query/key lengths) writes zeros
+    OStage::store(ost, rdq, (uint32_t)q0, row_bytes, 0, lane);
   }
 }
 

@@ -825,19 +825,32 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
     end_tile(j);
   }
 
+  // O leaves through the ring's LDS (not the descale slot after it), each wave in its own
+  // area, in as many column parts as the ring needs for the 16-bit rows (two at d = 128):
+  // the last end_tile() waited for every DMA and passed a barrier after every wave's last
+  // operand read.
+  constexpr int RING = NS * TB + VS * TBV;
+  constexpr int OPARTS = kWaves * RowStage<2 * D>::BYTES <= RING ? 1 : kWaves * RowStage<D>::BYTES <= RING ? 2 : 4;
+  using OStage = RowStage<2 * D / OPARTS>;
+  static_assert(kQW8 == 32 && NDB % OPARTS == 0 && kWaves * OStage::BYTES <= RING, "O staging fits the ring");
   if (nkt_w > 0) {
     const float l_tot = xhalf_sum(l_run);
     const float fac = dvm / kPScale / l_rnd;
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    char* ost = smem + wave * OStage::BYTES;
 #pragma unroll
-    for (int i = 0; i < NDB; ++i)
+    for (int part = 0; part < OPARTS; ++part) {
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int d0 = i * 32 + 8 * rr + 4 * hf;
-        const u32x2 v = {pack2<OUT_BF16>(oacc[i][4 * rr + 0] * fac, oacc[i][4 * rr + 1] * fac),
-                         pack2<OUT_BF16>(oacc[i][4 * rr + 2] * fac, oacc[i][4 * rr + 3] * fac)};
-        buf_store8(ro, (uint32_t)qrow * orow + d0 * 2, v);
-      }
+      for (int i = part * (NDB / OPARTS); i < (part + 1) * (NDB / OPARTS); ++i)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int d0 = i * 32 + 8 * rr + 4 * hf;
+          const u32x2 v = {pack2<OUT_BF16>(oacc[i][4 * rr + 0] * fac, oacc[i][4 * rr + 1] * fac),
+                           pack2<OUT_BF16>(oacc[i][4 * rr + 2] * fac, oacc[i][4 * rr + 3] * fac)};
+          OStage::put(ost, l32, (d0 - part * (D / OPARTS)) * 2, v);
+        }
+      OStage::store(ost, ro, (uint32_t)q0, orow, part * (2 * D / OPARTS), lane);
+    }
     if (hf == 0 && qrow < N) p.lse[((size_t)b * H + h) * N + qrow] = (m_use + fast_log2(l_tot)) * kLn2;
   }
 }

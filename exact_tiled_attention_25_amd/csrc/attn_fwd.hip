@@ -471,10 +471,15 @@ __global__ __launch_bounds__((fwd_threads<D, SMALL>()), (fwd_wgs<D, SMALL>())) v
     }
     return;
   }
+  // O leaves through the ring's LDS, each wave in its own area: the last end_tile() waited for
+  // every DMA and passed a barrier after every wave's last operand read.
+  using OStage = RowStage<2 * D>;
+  static_assert(kQW == 32 && kWaves * OStage::BYTES <= (int)sizeof(smem), "O staging fits the ring");
   if (nkt_w > 0) {
     const float l_tot = xhalf_sum(l_run);
     const float inv = 1.0f / l_tot;
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    char* ost = smem + wave * OStage::BYTES;
 #pragma unroll
     for (int i = 0; i < NDB; ++i)
 #pragma unroll
@@ -482,8 +487,9 @@ __global__ __launch_bounds__((fwd_threads<D, SMALL>()), (fwd_wgs<D, SMALL>())) v
         const int d0 = i * 32 + 8 * rr + 4 * hf;
         u32x2 v = {pack2<BF16>(oacc[i][4 * rr + 0] * inv, oacc[i][4 * rr + 1] * inv),
                    pack2<BF16>(oacc[i][4 * rr + 2] * inv, oacc[i][4 * rr + 3] * inv)};
-        buf_store8(ro, (uint32_t)qrow * row_bytes + d0 * 2, v);
+        OStage::put(ost, l32, d0 * 2, v);
       }
+    OStage::store(ost, ro, (uint32_t)q0, row_bytes, 0, lane);
     if (hf == 0 && qrow < N) p.lse[stat_row(p.cu, p.T, b, H, h, sv) + qrow] = (m_use + fast_log2(l_tot)) * kLn2;
   }
 }

@@ -166,6 +166,38 @@ __device__ __forceinline__ int v_lane_off(int lane) { return tr_lane_off<v_pitch
 template <int D>
 __device__ __forceinline__ u32x4 lds_vt(const char* lane_base, int c, int i) { return lds_tr<v_pitch<D>()>(lane_base, c, i); }
 
+// Output tile of one wave (32 rows of RB bytes: the 16-bit rows of O, dQ, dK or dV) written
+// through LDS. The MFMA accumulator hands each lane 8-byte pieces of one row, so a store
+// straight from it makes every instruction touch 32 rows, 16 bytes of each. Staged in the
+// wave's own LDS area (pitch RB + 16: the 32 rows of one piece write fall on 16 bank offsets,
+// two rows each, the least a 512-byte write can take) and read back as 16-byte row chunks,
+// each store instruction writes RB-byte rows whole (64 x 16 bytes). The stores carry the
+// non-temporal hint (cache-policy bit 1 of a buffer instruction): no kernel here reads its
+// own output again. Rows past the end of the buffer resource are dropped by its range check.
+template <int RB>
+struct RowStage {
+  static constexpr int PITCH = RB + 16;
+  static constexpr int BYTES = 32 * PITCH;
+  static constexpr int CPR = RB / 16;   // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;  // rows per store instruction
+  static_assert(RB % 16 == 0 && 64 % CPR == 0, "whole rows per store instruction");
+  // the piece of `row` at byte `byte` (8 bytes)
+  __device__ static __forceinline__ void put(char* st, int row, int byte, u32x2 v) {
+    *(u32x2*)(st + row * PITCH + byte) = v;
+  }
+  // rows 0..31 of the staged tile to bytes col0 .. col0 + RB - 1 of rows row0.. of the
+  // buffer (row_bytes apart); a kernel short of LDS stages its rows in column parts
+  __device__ static __forceinline__ void store(const char* st, __amdgpu_buffer_rsrc_t r, uint32_t row0,
+                                               uint32_t row_bytes, uint32_t col0, int lane) {
+#pragma unroll
+    for (int k = 0; k < 32 / RPI; ++k) {
+      const int row = k * RPI + lane / CPR, c = lane % CPR;
+      __builtin_amdgcn_raw_buffer_store_b128(*(const u32x4*)(st + row * PITCH + c * 16), r,
+                                             (row0 + row) * row_bytes + col0 + c * 16, 0, 2);
+    }
+  }
+};
+
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Wait until at most N of this wave's vector-memory operations are outstanding (the N most
 // recent ones may stay in flight across the following barrier).
