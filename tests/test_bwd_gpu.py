@@ -112,3 +112,27 @@ def test_bwd_ragged_default_form_one_head(lib, dtype, causal):
     b, h = 1, 9
     ref = oracle.head_backward(x["q"][b, :, h], x["k"][b, :, h], x["v"][b, :, h], x["do"][b, :, h], causal)
     _check((dq[b, :, h], dk[b, :, h], dv[b, :, h]), ref, f"ragged b={b} h={h}")
+
+
+@pytest.mark.parametrize("shape", [(1, 150, 2, 128), (2, 333, 2, 64), (1, 77, 2, 256)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_bwd_writes_nothing_outside_gradients(lib, shape, causal):
+    """Canary bytes around dQ, dK and dV stay untouched: each wave writes whole 32-row tiles
+    of them through LDS and relies on the buffer range check to drop the rows past N."""
+    from exact_tiled_attention_25_amd import binding
+    B, N, H, d = shape
+    log(f"bwd canary {shape} causal={causal}")
+    x = workloads.make_inputs(B, N, H, d, "bf16", 34, with_do=True)
+    q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
+    o, lse = binding.attn_fwd(q, k, v, causal)
+    pad, n = 4096, B * N * H * d
+    bufs = [torch.full((2 * pad + n,), 7.0, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    dq, dk, dv = (b[pad:pad + n].view(B, N, H, d) for b in bufs)
+    binding.attn_bwd(q, k, v, o, lse, do, causal, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    for name, b in zip(("dq", "dk", "dv"), bufs):
+        assert torch.all(b[:pad] == 7.0) and torch.all(b[-pad:] == 7.0), name
+    ref = binding.attn_bwd(q, k, v, o, lse, do, causal)
+    for a, r in zip((dq, dk, dv), ref):
+        assert torch.equal(a, r)

@@ -280,3 +280,26 @@ def test_fp8_full_size_matches_kernel_model(lib, name, causal):
     heads = [(0, 0), (B - 1, H - 1), (int(rng.integers(B)), int(rng.integers(H)))]
     rows = np.concatenate([[0, N - 1], rng.choice(N, 10, replace=False)])
     _model_check(o, lse, codes, causal, scale, heads, rows, "bf16", emul=_emulator(codes, causal, scale))
+
+
+@pytest.mark.parametrize("shape", [(1, 150, 2, 64), (1, 333, 2, 128), (1, 77, 2, 256)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_fp8_writes_nothing_outside_outputs(lib, shape):
+    """Canary bytes around O and LSE stay untouched: the epilogue writes whole rows (in two
+    column halves at d = 128) and relies on the buffer range check to drop the rows past N."""
+    B, N, H, d = shape
+    log(f"fp8 canary {shape}")
+    x = workloads.make_inputs(B, N, H, d, "bf16", 47)
+    g = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in _codes_for(x)]
+    pad, n = 4096, B * N * H * d
+    o_buf = torch.full((2 * pad + n,), 7.0, dtype=torch.bfloat16, device="cuda")
+    l_buf = torch.full((2 * pad + B * H * N,), 7.0, dtype=torch.float32, device="cuda")
+    o = o_buf[pad:pad + n].view(B, N, H, d)
+    lse = l_buf[pad:pad + B * H * N].view(B, H, N)
+    for causal in (False, True):
+        _binding().attn_fwd_fp8(*g, causal, scale=1 / np.sqrt(d), hadamard_seed=0, o=o, lse=lse)
+        torch.cuda.synchronize()
+        assert torch.all(o_buf[:pad] == 7.0) and torch.all(o_buf[-pad:] == 7.0)
+        assert torch.all(l_buf[:pad] == 7.0) and torch.all(l_buf[-pad:] == 7.0)
+        o_ref, l_ref = _binding().attn_fwd_fp8(*g, causal, scale=1 / np.sqrt(d), hadamard_seed=0)
+        assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)

@@ -106,10 +106,17 @@ def test_fwd_is_deterministic(lib):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_fwd_writes_nothing_outside_outputs(lib):
-    """Canary bytes around O and LSE stay untouched (ragged N exercises the tail tiles)."""
-    log("fwd canary")
-    B, N, H, d = 1, 150, 2, 128
+# (B, N, H, d): the short-grid form at d = 128 and 64, the default 8-wave form (N > 1024 and at
+# least 256 workgroups), and the 4-wave form at d = 256; every N ragged
+CANARY = [(1, 150, 2, 128), (2, 333, 2, 64), (4, 1100, 16, 128), (1, 300, 2, 256)]
+
+
+@pytest.mark.parametrize("shape", CANARY, ids=lambda s: "x".join(map(str, s)))
+def test_fwd_writes_nothing_outside_outputs(lib, shape):
+    """Canary bytes around O and LSE stay untouched: the epilogue writes whole 32-row tiles
+    and relies on the buffer range check to drop the rows past N."""
+    B, N, H, d = shape
+    log(f"fwd canary {shape}")
     x = workloads.make_inputs(B, N, H, d, "bf16", 22)
     from exact_tiled_attention_25_amd import binding
     pad = 4096
