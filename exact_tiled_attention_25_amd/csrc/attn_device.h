@@ -40,14 +40,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
-__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
-  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
-}
 __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
-}
-__device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
-  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
 }
 
 // 32x32x16 MFMA on 16-bit inputs held as 4 dwords per lane.
@@ -149,8 +143,6 @@ __device__ __forceinline__ void settle(const T& x) {
 __device__ __forceinline__ void pin_acc(f32x16& x) { asm volatile("" : "+a"(x)); }
 // ... and an MFMA operand held in registers for a whole loop (MFMAs read AGPR operands).
 __device__ __forceinline__ void pin_acc(u32x4& x) { asm volatile("" : "+a"(x)); }
-// An MFMA result that the VALU consumes next stays in VGPRs.
-__device__ __forceinline__ void pin_vgpr(f32x16& x) { asm volatile("" : "+v"(x)); }
 
 // Sequence b of a batch: its first token row and its length. Fixed-length batches (cu =
 // null): b * N and N. Variable-length batches: cu_seqlens[b] and cu_seqlens[b+1] - that.
