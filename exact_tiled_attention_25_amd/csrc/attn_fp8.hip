@@ -319,7 +319,11 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
   // One LDS array: the ring stages, then a slot for the per-wave maxima of the V descales.
   // (With a second __shared__ variable the compiler gives every access to this one the same
   // alias scope, loses the restrict scopes below, and waits for all DMA before LDS reads.)
-  __shared__ __attribute__((aligned(1024))) char smem[NS * TB + VS * TBV + 4 * kWaves];
+  // Then the tile descriptor table (below) in the rest of the CU's 160 KiB.
+  constexpr int DT_OFF = NS * TB + VS * TBV + 4 * kWaves;
+  constexpr int DT_MAX = (160 * 1024 - DT_OFF) / 16;
+  static_assert(DT_OFF % 16 == 0 && DT_MAX > 0, "descriptor table placement");
+  __shared__ __attribute__((aligned(1024))) char smem[DT_OFF + 16 * DT_MAX];
   float* const red = (float*)(smem + NS * TB + VS * TBV);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -414,7 +418,7 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
     dk = dk_s[t];
     dv = dv_s[t];
   };
-  float dk_c, dv_c;   // descales of the tile the next iteration exponentiates
+  float dk_c, dv_c;   // descales of tile 0 (later tiles: tile_desc below)
   load_desc(0, dk_c, dv_c);
   // The weight 64 * dv/dv_max of a tile's P~ is split as 2^e * w, w in [32, 64): w enters the
   // exp2 argument as its log2 (so every tile's e4m3 operand P~ w spans the same range, whatever
@@ -435,12 +439,41 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
     rw = __builtin_amdgcn_rcpf(w);
   };
   auto set_weight = [&](float dv) { weight_of(dv, logw_c, rw_c, sc_c); };
+  // Tile descriptors: the K descale and the V weight split (log2 w, 1/w, code) of every key
+  // tile, formed once per workgroup into the LDS after the ring when the head's tiles fit
+  // (then a tile costs one broadcast 16-byte read instead of two scalar loads, a frexp pair, a
+  // log2 and a reciprocal), else formed per tile as the iterations need them.
+  f32x4* const dtab = (f32x4*)(smem + DT_OFF);
+  const bool use_dtab = nkt <= DT_MAX;
+  auto tile_desc = [&](int t, float& dk, float& logw, float& rw, int& code) {
+    if (use_dtab) {
+      const f32x4 v = dtab[t];
+      dk = v[0];
+      logw = v[1];
+      rw = v[2];
+      code = __float_as_int(v[3]);
+    } else {
+      float dv;
+      load_desc(t, dk, dv);
+      weight_of(dv, logw, rw, code);
+    }
+  };
 
   dma_k(0);
 #pragma unroll
   for (int t = 0; t <= NS - 2; ++t) {
     if (t < nkt) dma_v(t);
     if (t + 1 < nkt) dma_k(t + 1);
+  }
+  // the descriptor table, published by the barrier before the first tile (its loads are
+  // issued after the first tiles' DMA, so waiting for them holds nothing else up)
+  if (use_dtab) {
+    for (int t = tid; t < nkt; t += 64 * kWaves) {
+      float lw, rwt;
+      int code;
+      weight_of(dv_h[t], lw, rwt, code);
+      dtab[t] = f32x4{dk_h[t], lw, rwt, __int_as_float(code)};
+    }
   }
   // Q (and its descale) waited for here, not inside the tile loop, and only now: the load
   // and the first tiles' DMA share one HBM round trip
@@ -552,7 +585,8 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
   constexpr int EPS2 = 16 / (S2 - MS);                   // first-block exponentials per later step
   static_assert(NKB == 2 && EPS * S1 == 16 && MPS * MS == 16 * NKB && MPS % 2 == 0 && S2 > MS &&
                 EPS2 * (S2 - MS) == 16 && EPS2 % 4 == 0, "step split");
-  float dk_n, dv_n;
+  float dk_n, logw_n, rw_n;   // the next tile's descriptor
+  int sc_n;
   // P~ operands. Kept across tiles: each conversion writes half of a word whose other half it
   // keeps, and the word it lands in belongs to a tile already consumed, so no register has to
   // be cleared first. The ping-pong form uses pka only; the split form alternates pka and pkb
@@ -565,7 +599,7 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
   // every outstanding DMA before the first read, which drains the ring's prefetch each tile).
   auto fast_iter_pp = [&](auto late, int jj, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB], const char* __restrict__ kn,
                        const char* __restrict__ vc, char* __restrict__ kd, char* __restrict__ vd) __attribute__((always_inline)) {
-    load_desc(jj + 1 < nkt ? jj + 1 : jj, dk_n, dv_n);
+    tile_desc(jj + 1 < nkt ? jj + 1 : jj, dk_n, logw_n, rw_n, sc_n);
     if (jj + NS - 1 < nkt) dma_issue<VPlan, kWaves>(vvoff, vd, vbase, (jj + NS - 1) * BC, row_bytes, nrec, wave);
     if (jj + NS < nkt) dma_issue<Plan, kWaves>(voff, kd, kbase, (jj + NS) * BC, row_bytes, nrec, wave);
     rescale();
@@ -619,22 +653,19 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
     mx = xhalf_max(mx);
     mx_next = mx * coef_n;
     coef_c = coef_n;
-    dk_c = dk_n;
-    dv_c = dv_n;
-    set_weight(dv_c);
+    logw_c = logw_n;
+    rw_c = rw_n;
+    sc_c = sc_n;
     if constexpr (!decltype(late)::value) end_tile(jj);
   };
   // The split form's iteration (same operands).
   auto fast_iter = [&](auto late, int jj, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB], i32x8& pkc, i32x8& pkn,
                        const char* __restrict__ kn, const char* __restrict__ vc, char* __restrict__ kd,
                        char* __restrict__ vd) __attribute__((always_inline)) {
-    load_desc(jj + 1 < nkt ? jj + 1 : jj, dk_n, dv_n);
+    tile_desc(jj + 1 < nkt ? jj + 1 : jj, dk_n, logw_n, rw_n, sc_n);
     if (jj + NS - 1 < nkt) dma_issue<VPlan, kWaves>(vvoff, vd, vbase, (jj + NS - 1) * BC, row_bytes, nrec, wave);
     if (jj + NS < nkt) dma_issue<Plan, kWaves>(voff, kd, kbase, (jj + NS) * BC, row_bytes, nrec, wave);
     const float coef_n = cq * dk_n;
-    float logw_n, rw_n;
-    int sc_n;
-    weight_of(dv_n, logw_n, rw_n, sc_n);
     i32x8 kop[S1];
     float e[16];
     float psum_a = 0.f, psum_b = 0.f;
@@ -723,8 +754,6 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
     logw_c = logw_n;
     rw_c = rw_n;
     sc_c = sc_n;
-    dk_c = dk_n;
-    dv_c = dv_n;
     if constexpr (!decltype(late)::value) end_tile(jj);
   };
   int j = 0;
@@ -780,7 +809,7 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
   // iterations, tile j has its reference set and its first key block in pka.
   bool half = !PP && j > 0;
   for (; j < nkt; ++j) {
-    load_desc(j + 1 < nkt ? j + 1 : j, dk_n, dv_n);
+    tile_desc(j + 1 < nkt ? j + 1 : j, dk_n, logw_n, rw_n, sc_n);
     prefetch(j);
     if (j < nkt_w) {
       if (!half) rescale();
@@ -818,9 +847,9 @@ __global__ __launch_bounds__(64 * Fp8Cfg<D>::WAVES, 1) void fwd_fp8_kernel(Fp8Fw
       }
     }
     coef_c = cq * dk_n;
-    dk_c = dk_n;
-    dv_c = dv_n;
-    set_weight(dv_c);
+    logw_c = logw_n;
+    rw_c = rw_n;
+    sc_c = sc_n;
     half = false;
     end_tile(j);
   }
