@@ -15,6 +15,6 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def lib():
-    """The loaded C-ABI library; on a GPU machine a missing build is an error, not a skip."""
+    """The loaded C-ABI library; on a machine with the GPU a missing build is an error, not a skip."""
     from exact_tiled_attention_25_amd import binding
     return binding.load()
